@@ -1,0 +1,290 @@
+"""Python binding of libcosa, the MI355X CoSA prefill-attention library.
+
+Argument marshalling only: every computation runs in the HIP kernels of
+``libcosa.so`` (built in-tree by ``block_sparse_attention_26_amd.build``).
+There is no fallback: if the library is missing or fails to load, every entry
+point raises.
+
+Low-level functions carry the C names (``cosa_kap_order``,
+``cosa_osk_attention``, ``cosa_dense_attention``, ``cosa_validate``,
+``cosa_dims``, ``cosa_kap_workspace_size``) and take integer device pointers.
+The ``Problem`` class and the ``kap_order`` / ``osk_attention`` /
+``dense_attention`` helpers accept torch tensors that already live on the GPU
+and allocate the outputs with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+__all__ = [
+    "CosaError", "Problem", "load", "library_path",
+    "cosa_validate", "cosa_dims", "cosa_kap_workspace_size", "cosa_kap_order",
+    "cosa_osk_attention", "cosa_dense_attention", "cosa_status_string",
+    "cosa_last_error", "cosa_version",
+    "kap_order", "osk_attention", "dense_attention",
+    "COSA_F32", "COSA_BF16", "EXPORTED_SYMBOLS",
+]
+
+COSA_F32, COSA_BF16 = 0, 1
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+# Every symbol include/cosa.h declares.
+EXPORTED_SYMBOLS = (
+    "cosa_validate", "cosa_dims", "cosa_kap_workspace_size", "cosa_kap_order",
+    "cosa_osk_attention", "cosa_dense_attention", "cosa_status_string",
+    "cosa_last_error", "cosa_version",
+)
+
+
+class CosaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libcosa status {status}: {message}")
+        self.status = status
+
+
+class cosa_problem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("num_pages", ctypes.c_int32),
+        ("max_blocks_k", ctypes.c_int32),
+        ("cu_seqlens_q", ctypes.c_void_p), ("seqlens_k", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("host_cu_seqlens_q", ctypes.c_void_p), ("host_seqlens_k", ctypes.c_void_p),
+    ]
+
+
+class cosa_dims_t(ctypes.Structure):
+    _fields_ = [("total_q", ctypes.c_int32), ("max_nq", ctypes.c_int32),
+                ("max_nk", ctypes.c_int32), ("max_nr", ctypes.c_int32),
+                ("kmax", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return os.environ.get("COSA_LIBRARY", os.path.join(_PKG, "libcosa.so"))
+
+
+def load():
+    """Load libcosa.so (once). Raises if it is not built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"libcosa.so not found at {path}; build it with "
+            "`python -m block_sparse_attention_26_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(cosa_problem)
+    vp, i32, f32, f64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
+    sigs = {
+        "cosa_validate": (i32, [P]),
+        "cosa_dims": (i32, [P, i32, f64, ctypes.POINTER(cosa_dims_t)]),
+        "cosa_kap_workspace_size": (sz, [P, i32, i32]),
+        "cosa_kap_order": (i32, [P, vp, vp, i32, f64, vp, vp, vp, i32, vp, vp, vp, sz, vp]),
+        "cosa_osk_attention": (i32, [P, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp, vp, vp, vp, vp]),
+        "cosa_dense_attention": (i32, [P, vp, vp, vp, vp, vp, vp]),
+        "cosa_status_string": (ctypes.c_char_p, [i32]),
+        "cosa_last_error": (ctypes.c_char_p, []),
+        "cosa_version": (i32, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = load()
+        raise CosaError(status, lib.cosa_last_error().decode())
+
+
+# ---- raw C entry points (same names as include/cosa.h) ---------------------
+
+def cosa_status_string(status: int) -> str:
+    return load().cosa_status_string(status).decode()
+
+
+def cosa_last_error() -> str:
+    return load().cosa_last_error().decode()
+
+
+def cosa_version() -> int:
+    return load().cosa_version()
+
+
+def cosa_validate(problem: "cosa_problem") -> int:
+    return load().cosa_validate(ctypes.byref(problem))
+
+
+def cosa_dims(problem: "cosa_problem", pool: int, budget: float) -> "cosa_dims_t":
+    d = cosa_dims_t()
+    _check(load().cosa_dims(ctypes.byref(problem), int(pool), float(budget), ctypes.byref(d)))
+    return d
+
+
+def cosa_kap_workspace_size(problem: "cosa_problem", pool: int, with_scores: bool) -> int:
+    return load().cosa_kap_workspace_size(ctypes.byref(problem), int(pool), 1 if with_scores else 0)
+
+
+def cosa_kap_order(problem, q, k_pages, pool, budget, order, hrm, count, kmax,
+                   proxy_scores, block_scores, workspace, workspace_bytes, stream) -> None:
+    _check(load().cosa_kap_order(ctypes.byref(problem), q, k_pages, int(pool), float(budget),
+                                 order, hrm, count, int(kmax), proxy_scores, block_scores,
+                                 workspace, int(workspace_bytes), stream))
+
+
+def cosa_osk_attention(problem, q, k_pages, v_pages, order, count, kmax, group,
+                       skip_threshold, o, visited, skipped, skip_bits, lse, stream) -> None:
+    _check(load().cosa_osk_attention(ctypes.byref(problem), q, k_pages, v_pages, order, count,
+                                     int(kmax), int(group), float(skip_threshold), o, visited,
+                                     skipped, skip_bits, lse, stream))
+
+
+def cosa_dense_attention(problem, q, k_pages, v_pages, o, lse, stream) -> None:
+    _check(load().cosa_dense_attention(ctypes.byref(problem), q, k_pages, v_pages, o, lse, stream))
+
+
+# ---- torch-facing helpers ---------------------------------------------------
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+class Problem:
+    """A cosa_problem plus the device and host metadata it points at.
+
+    ``cu_seqlens_q`` / ``seqlens_k`` / ``block_table`` are int32 device
+    tensors; ``host_cu_seqlens_q`` / ``host_seqlens_k`` are the same values as
+    Python sequences (they are copied into host arrays owned here).
+    """
+
+    def __init__(self, *, h_q: int, h_kv: int, head_dim: int, block: int, dtype: int,
+                 softmax_scale: float, num_pages: int, cu_seqlens_q, seqlens_k, block_table,
+                 host_cu_seqlens_q: Sequence[int], host_seqlens_k: Sequence[int]):
+        batch = len(host_seqlens_k)
+        self._hcu = (ctypes.c_int32 * (batch + 1))(*[int(x) for x in host_cu_seqlens_q])
+        self._hlk = (ctypes.c_int32 * batch)(*[int(x) for x in host_seqlens_k])
+        self._dev = (cu_seqlens_q, seqlens_k, block_table)  # keep alive
+        self.c = cosa_problem(
+            batch=batch, h_q=h_q, h_kv=h_kv, head_dim=head_dim, block=block, dtype=dtype,
+            softmax_scale=softmax_scale, num_pages=num_pages,
+            max_blocks_k=int(block_table.shape[1]),
+            cu_seqlens_q=cu_seqlens_q.data_ptr(), seqlens_k=seqlens_k.data_ptr(),
+            block_table=block_table.data_ptr(),
+            host_cu_seqlens_q=ctypes.cast(self._hcu, ctypes.c_void_p),
+            host_seqlens_k=ctypes.cast(self._hlk, ctypes.c_void_p),
+        )
+        self.group = h_q // h_kv
+
+    @classmethod
+    def from_case(cls, case, device="cuda"):
+        """Build from a ``synthetic.Case``, copying its metadata to the device."""
+        dt = COSA_BF16 if case.dtype == "bf16" else COSA_F32
+        return cls(h_q=case.h_q, h_kv=case.h_kv, head_dim=case.head_dim, block=case.block,
+                   dtype=dt, softmax_scale=case.scale, num_pages=int(case.k_pages.shape[0]),
+                   cu_seqlens_q=case.cu_seqlens_q.to(device), seqlens_k=case.seqlens_k.to(device),
+                   block_table=case.block_table.to(device),
+                   host_cu_seqlens_q=case.cu_seqlens_q.tolist(),
+                   host_seqlens_k=case.seqlens_k.tolist())
+
+    def dims(self, pool: int = 0, budget: float = 0.0) -> cosa_dims_t:
+        return cosa_dims(self.c, pool, budget)
+
+    def validate(self) -> int:
+        return cosa_validate(self.c)
+
+
+def kap_order(problem: Problem, q, k_pages, pool: int, budget: float, *, kmax=None,
+              export_scores: bool = False, export_block_scores: bool = False,
+              workspace=None, stream=None):
+    """Run the proxy; returns dict(order, hrm, count, kmax[, P][, s])."""
+    import torch
+    dev = q.device
+    d = problem.dims(pool, budget)
+    kmax = d.kmax if kmax is None else int(kmax)
+    order = torch.empty((problem.c.batch, problem.c.h_kv, d.max_nq, kmax), dtype=torch.int32, device=dev)
+    hrm = torch.empty(order.shape, dtype=torch.uint8, device=dev)
+    count = torch.empty(order.shape[:3], dtype=torch.int32, device=dev)
+    P = (torch.empty((problem.c.batch, problem.c.h_q, d.max_nr, d.max_nk), dtype=torch.float32, device=dev)
+         if export_scores else None)
+    s = (torch.empty((problem.c.batch, problem.c.h_kv, d.max_nq, d.max_nk), dtype=torch.float32, device=dev)
+         if export_block_scores else None)
+    ws_bytes = cosa_kap_workspace_size(problem.c, pool, P is None)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    cosa_kap_order(problem.c, q.data_ptr(), k_pages.data_ptr(), pool, budget, order.data_ptr(),
+                   hrm.data_ptr(), count.data_ptr(), kmax, _ptr(P), _ptr(s), workspace.data_ptr(),
+                   workspace.numel(), _stream(stream))
+    out = {"order": order, "hrm": hrm, "count": count, "kmax": kmax, "workspace": workspace}
+    if P is not None:
+        out["P"] = P
+    if s is not None:
+        out["s"] = s
+    return out
+
+
+def osk_attention(problem: Problem, q, k_pages, v_pages, order, count, tau: float, *,
+                  skip_bits: bool = False, lse: bool = False, out=None, stream=None):
+    """Run the ordered-skipping kernel; returns dict(O, visited, skipped[, skip_bits][, lse])."""
+    import torch
+    dev = q.device
+    d = problem.dims()
+    kmax = int(order.shape[3])
+    o = torch.empty_like(q) if out is None else out
+    vis = torch.empty((problem.c.batch, problem.c.h_q, d.max_nq), dtype=torch.int32, device=dev)
+    skp = torch.empty_like(vis)
+    bits = (torch.empty((problem.c.batch, problem.c.h_q, d.max_nq, kmax), dtype=torch.uint8, device=dev)
+            if skip_bits else None)
+    ls = torch.empty((problem.c.h_q, d.total_q), dtype=torch.float32, device=dev) if lse else None
+    cosa_osk_attention(problem.c, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                       order.data_ptr(), count.data_ptr(), kmax, problem.group, tau, o.data_ptr(),
+                       vis.data_ptr(), skp.data_ptr(), _ptr(bits), _ptr(ls), _stream(stream))
+    res = {"O": o, "visited": vis, "skipped": skp}
+    if bits is not None:
+        res["skip_bits"] = bits
+    if ls is not None:
+        res["lse"] = ls
+    return res
+
+
+def dense_attention(problem: Problem, q, k_pages, v_pages, *, lse: bool = False, out=None,
+                    stream=None):
+    """Dense causal attention; returns dict(O[, lse])."""
+    import torch
+    d = problem.dims()
+    o = torch.empty_like(q) if out is None else out
+    ls = torch.empty((problem.c.h_q, d.total_q), dtype=torch.float32, device=q.device) if lse else None
+    cosa_dense_attention(problem.c, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                         o.data_ptr(), _ptr(ls), _stream(stream))
+    res = {"O": o}
+    if ls is not None:
+        res["lse"] = ls
+    return res
+
+
+def dense_causal_flops(seqlens_q: Sequence[int], seqlens_k: Sequence[int], h_q: int, head_dim: int) -> float:
+    """4 * d * (number of causal (query, key) pairs) * h_q: QK^T and PV of dense attention."""
+    pairs = 0
+    for lq, lk in zip(seqlens_q, seqlens_k):
+        off = lk - lq
+        pairs += lq * (off + 1) + lq * (lq - 1) // 2
+    return 4.0 * head_dim * pairs * h_q
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,292 @@
+// Host side of libcosa: argument validation, closed-form extents, workspace
+// layout and kernel launches. Declarations and contracts: include/cosa.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/cosa.h"
+#include "cosa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+cosa_status fail(cosa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+cosa_status ok() {
+  g_last_error.clear();
+  return COSA_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Budget rule: k = clamp(ceil(beta * n - 1e-9), 1, n) in IEEE double.
+int budget_count(int n, double beta) {
+  int k = (int)ceil(beta * (double)n - 1e-9);
+  return std::max(1, std::min(n, k));
+}
+
+// Causal KV blocks of query block qb (kb = 0 .. n-1).
+int n_causal(int qb, int B, int Lq, int Lk) {
+  const int off = Lk - Lq;
+  return (off + std::min(qb * B + B - 1, Lq - 1)) / B + 1;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+cosa_status validate(const cosa_problem* p) {
+  if (!p) return fail(COSA_ERR_INVALID_ARG, "problem is NULL");
+  if (p->batch < 1) return fail(COSA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", p->batch);
+  if (p->h_q < 1 || p->h_kv < 1)
+    return fail(COSA_ERR_INVALID_ARG, "h_q and h_kv must be >= 1 (got %d, %d)", p->h_q, p->h_kv);
+  if (p->h_q % p->h_kv != 0)
+    return fail(COSA_ERR_INVALID_ARG, "h_kv (%d) must divide h_q (%d)", p->h_kv, p->h_q);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(COSA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
+  if (p->block != 64 && p->block != 128)
+    return fail(COSA_ERR_UNSUPPORTED, "block must be 64 or 128 (got %d)", p->block);
+  if (p->dtype != COSA_F32 && p->dtype != COSA_BF16)
+    return fail(COSA_ERR_INVALID_ARG, "dtype must be COSA_F32 or COSA_BF16 (got %d)", p->dtype);
+  if (!(p->softmax_scale > 0.f) || !isfinite(p->softmax_scale))
+    return fail(COSA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (p->num_pages < 1) return fail(COSA_ERR_INVALID_ARG, "num_pages must be >= 1");
+  if (p->max_blocks_k < 1) return fail(COSA_ERR_INVALID_ARG, "max_blocks_k must be >= 1");
+  if (!p->cu_seqlens_q || !p->seqlens_k || !p->block_table)
+    return fail(COSA_ERR_INVALID_ARG, "cu_seqlens_q, seqlens_k and block_table must be non-NULL");
+  if (!p->host_cu_seqlens_q || !p->host_seqlens_k)
+    return fail(COSA_ERR_INVALID_ARG, "host_cu_seqlens_q and host_seqlens_k must be non-NULL");
+  if (p->host_cu_seqlens_q[0] != 0) return fail(COSA_ERR_INVALID_ARG, "cu_seqlens_q[0] must be 0");
+  for (int b = 0; b < p->batch; ++b) {
+    const int64_t lq = (int64_t)p->host_cu_seqlens_q[b + 1] - p->host_cu_seqlens_q[b];
+    const int64_t lk = p->host_seqlens_k[b];
+    if (lq < 0) return fail(COSA_ERR_INVALID_ARG, "cu_seqlens_q decreases at sequence %d", b);
+    if (lk < lq)
+      return fail(COSA_ERR_INVALID_ARG, "sequence %d: seqlens_k (%lld) < query length (%lld)", b,
+                  (long long)lk, (long long)lq);
+    if (cdiv(lk, p->block) > p->max_blocks_k)
+      return fail(COSA_ERR_INVALID_ARG, "sequence %d needs %lld KV blocks > max_blocks_k (%d)", b,
+                  (long long)cdiv(lk, p->block), p->max_blocks_k);
+  }
+  return COSA_OK;
+}
+
+void compute_dims(const cosa_problem* p, int pool, double budget, cosa_dims_t* d) {
+  d->total_q = p->host_cu_seqlens_q[p->batch];
+  d->max_nq = d->max_nk = d->max_nr = 0;
+  d->kmax = 0;
+  for (int b = 0; b < p->batch; ++b) {
+    const int lq = p->host_cu_seqlens_q[b + 1] - p->host_cu_seqlens_q[b];
+    const int lk = p->host_seqlens_k[b];
+    const int nq = (int)cdiv(lq, p->block);
+    d->max_nq = std::max(d->max_nq, nq);
+    d->max_nk = std::max(d->max_nk, (int)cdiv(lk, p->block));
+    if (pool > 0) d->max_nr = std::max(d->max_nr, (int)cdiv(lq, pool));
+    if (budget > 0.0 && nq > 0)
+      d->kmax = std::max(d->kmax, budget_count(n_causal(nq - 1, p->block, lq, lk), budget));
+  }
+  if (budget > 0.0) d->kmax = std::max(d->kmax, 1);
+}
+
+cosa_status check_pool(const cosa_problem* p, int pool) {
+  if (pool < 1 || pool > p->block || p->block % pool != 0)
+    return fail(COSA_ERR_INVALID_ARG, "pool (%d) must divide block (%d)", pool, p->block);
+  return COSA_OK;
+}
+
+size_t kap_ws_size(const cosa_problem* p, int pool, bool with_scores) {
+  cosa_dims_t d;
+  compute_dims(p, pool, 0.0, &d);
+  const size_t es = p->dtype == COSA_BF16 ? 2 : 4;
+  size_t sz = align256((size_t)p->batch * d.max_nr * p->h_q * p->head_dim * es);
+  sz += align256((size_t)p->num_pages * p->h_kv * (p->block / pool) * p->head_dim * es);
+  if (with_scores) sz += align256((size_t)p->batch * p->h_q * d.max_nr * d.max_nk * sizeof(float));
+  return sz;
+}
+
+cosa::SeqArgs seq_args(const cosa_problem* p, const cosa_dims_t& d) {
+  cosa::SeqArgs s;
+  s.cu_seqlens_q = p->cu_seqlens_q;
+  s.seqlens_k = p->seqlens_k;
+  s.block_table = p->block_table;
+  s.batch = p->batch;
+  s.h_q = p->h_q;
+  s.h_kv = p->h_kv;
+  s.group = p->h_q / p->h_kv;
+  s.max_blocks_k = p->max_blocks_k;
+  s.num_pages = p->num_pages;
+  s.max_nq = d.max_nq;
+  s.max_nk = d.max_nk;
+  return s;
+}
+
+cosa_status hip_result(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(COSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+cosa_status run_attention(const cosa_problem* p, const void* q, const void* k, const void* v,
+                          const int32_t* order, const int32_t* count, int32_t kmax, int32_t group,
+                          float tau, void* o, int32_t* visited, int32_t* skipped,
+                          uint8_t* skip_bits, float* lse, void* stream, bool dense) {
+  cosa_status st = validate(p);
+  if (st != COSA_OK) return st;
+  if (!q || !k || !v || !o) return fail(COSA_ERR_INVALID_ARG, "q, k_pages, v_pages and o must be non-NULL");
+  if (!dense) {
+    if (!order || !count || !visited || !skipped)
+      return fail(COSA_ERR_INVALID_ARG, "order, count, visited and skipped must be non-NULL");
+    if (kmax < 1) return fail(COSA_ERR_INVALID_ARG, "kmax must be >= 1 (got %d)", kmax);
+    if (group != p->h_q / p->h_kv)
+      return fail(COSA_ERR_INVALID_ARG, "group (%d) must equal h_q / h_kv (%d)", group, p->h_q / p->h_kv);
+    if (!(tau >= 0.f && tau < 1.f))
+      return fail(COSA_ERR_INVALID_ARG, "skip_threshold must lie in [0, 1) (got %g)", (double)tau);
+  }
+  cosa_dims_t d;
+  compute_dims(p, 0, 0.0, &d);
+  if (d.total_q == 0 || d.max_nq == 0) return ok();
+  cosa::OskArgs a{};
+  a.seq = seq_args(p, d);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.order = order;
+  a.count = count;
+  a.visited = visited;
+  a.skipped = skipped;
+  a.skip_bits = skip_bits;
+  a.lse = lse;
+  a.total_q = d.total_q;
+  a.kmax = kmax;
+  a.scale = p->softmax_scale;
+  a.scale_log2 = (float)((double)p->softmax_scale * 1.4426950408889634);
+  a.skip_on = (!dense && tau > 0.f) ? 1 : 0;
+  a.skip_thr_raw = a.skip_on ? (float)(log((double)tau) / (double)p->softmax_scale) : 0.f;
+  a.n_units = (int64_t)p->batch * p->h_q * d.max_nq;
+  return hip_result(cosa::launch_osk(a, p->dtype, p->head_dim, p->block, dense, (hipStream_t)stream),
+                    dense ? "dense attention launch" : "OSK launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+cosa_status cosa_validate(const cosa_problem* problem) {
+  cosa_status st = validate(problem);
+  return st == COSA_OK ? ok() : st;
+}
+
+cosa_status cosa_dims(const cosa_problem* problem, int32_t pool, double budget, cosa_dims_t* out) {
+  cosa_status st = validate(problem);
+  if (st != COSA_OK) return st;
+  if (!out) return fail(COSA_ERR_INVALID_ARG, "out is NULL");
+  if (pool != 0 && (st = check_pool(problem, pool)) != COSA_OK) return st;
+  if (!(budget >= 0.0 && budget <= 1.0))
+    return fail(COSA_ERR_INVALID_ARG, "budget must lie in (0, 1] (or 0 to skip kmax)");
+  compute_dims(problem, pool, budget, out);
+  return ok();
+}
+
+size_t cosa_kap_workspace_size(const cosa_problem* problem, int32_t pool, int32_t with_scores) {
+  if (validate(problem) != COSA_OK || check_pool(problem, pool) != COSA_OK) return 0;
+  return kap_ws_size(problem, pool, with_scores != 0);
+}
+
+cosa_status cosa_kap_order(const cosa_problem* problem, const void* q, const void* k_pages,
+                           int32_t pool, double budget, int32_t* order, uint8_t* hrm,
+                           int32_t* count, int32_t kmax, float* proxy_scores,
+                           float* block_scores, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  cosa_status st = validate(problem);
+  if (st != COSA_OK) return st;
+  if ((st = check_pool(problem, pool)) != COSA_OK) return st;
+  if (!(budget > 0.0 && budget <= 1.0))
+    return fail(COSA_ERR_INVALID_ARG, "budget must lie in (0, 1] (got %g)", budget);
+  if (!q || !k_pages || !order || !hrm || !count)
+    return fail(COSA_ERR_INVALID_ARG, "q, k_pages, order, hrm and count must be non-NULL");
+  cosa_dims_t d;
+  compute_dims(problem, pool, budget, &d);
+  if (kmax < d.kmax)
+    return fail(COSA_ERR_INVALID_ARG, "kmax (%d) is smaller than the widest list (%d)", kmax, d.kmax);
+  if (d.max_nk > cosa::kMaxSortBlocks)
+    return fail(COSA_ERR_UNSUPPORTED, "max KV blocks per sequence %d exceeds %d", d.max_nk,
+                cosa::kMaxSortBlocks);
+  if ((int64_t)(problem->h_q / problem->h_kv) * (problem->block / pool) > 4096)
+    return fail(COSA_ERR_UNSUPPORTED, "group * block / pool exceeds 4096 pooled rows per list");
+  const bool own_scores = proxy_scores == nullptr;
+  const size_t need = kap_ws_size(problem, pool, own_scores);
+  if (!workspace || workspace_bytes < need)
+    return fail(COSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (((uintptr_t)workspace & 255) != 0)
+    return fail(COSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (d.total_q == 0 || d.max_nq == 0) return ok();
+
+  const size_t es = problem->dtype == COSA_BF16 ? 2 : 4;
+  unsigned char* ws = (unsigned char*)workspace;
+  cosa::KapArgs a{};
+  a.seq = seq_args(problem, d);
+  a.q = q;
+  a.k = k_pages;
+  a.q_pool = ws;
+  ws += align256((size_t)problem->batch * d.max_nr * problem->h_q * problem->head_dim * es);
+  a.k_pool = ws;
+  ws += align256((size_t)problem->num_pages * problem->h_kv * (problem->block / pool) *
+                 problem->head_dim * es);
+  a.scores = own_scores ? (float*)ws : proxy_scores;
+  a.fill_scores = own_scores ? 0 : 1;
+  a.block_scores = block_scores;
+  a.order = order;
+  a.hrm = hrm;
+  a.count = count;
+  a.pool = pool;
+  a.max_nr = d.max_nr;
+  a.kmax = kmax;
+  a.budget = budget;
+  a.scale = problem->softmax_scale;
+  return hip_result(cosa::launch_kap(a, problem->dtype, problem->head_dim, problem->block,
+                                     (hipStream_t)stream),
+                    "KAP launch");
+}
+
+cosa_status cosa_osk_attention(const cosa_problem* problem, const void* q, const void* k_pages,
+                               const void* v_pages, const int32_t* order, const int32_t* count,
+                               int32_t kmax, int32_t group, float skip_threshold, void* o,
+                               int32_t* visited, int32_t* skipped, uint8_t* skip_bits, float* lse,
+                               void* stream) {
+  return run_attention(problem, q, k_pages, v_pages, order, count, kmax, group, skip_threshold, o,
+                       visited, skipped, skip_bits, lse, stream, false);
+}
+
+cosa_status cosa_dense_attention(const cosa_problem* problem, const void* q, const void* k_pages,
+                                 const void* v_pages, void* o, float* lse, void* stream) {
+  return run_attention(problem, q, k_pages, v_pages, nullptr, nullptr, 1,
+                       problem ? problem->h_q / std::max(problem->h_kv, 1) : 1, 0.f, o, nullptr,
+                       nullptr, nullptr, lse, stream, true);
+}
+
+const char* cosa_status_string(cosa_status status) {
+  switch (status) {
+    case COSA_OK: return "success";
+    case COSA_ERR_INVALID_ARG: return "invalid argument";
+    case COSA_ERR_UNSUPPORTED: return "unsupported size or layout";
+    case COSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case COSA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* cosa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t cosa_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal interface between the C-ABI host layer (cosa_api.cpp) and the HIP
+// kernels (osk.hip, kap.hip). Not installed; the public ABI is include/cosa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cosa {
+
+// Workgroups are dispatched round-robin over the MI355X's 8 XCDs (each with
+// its own L2); launch mappings group units that share K/V pages per XCD.
+constexpr int kNumXcd = 8;
+
+// Largest KV-block count per sequence the proxy's in-LDS sort handles.
+constexpr int kMaxSortBlocks = 4096;
+
+struct SeqArgs {
+  const int32_t* cu_seqlens_q;  // [batch+1]
+  const int32_t* seqlens_k;     // [batch]
+  const int32_t* block_table;   // [batch, max_blocks_k]
+  int32_t batch, h_q, h_kv, group, max_blocks_k, num_pages;
+  int32_t max_nq, max_nk;
+};
+
+// Ordered-skip / dense attention launch.
+struct OskArgs {
+  SeqArgs seq;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const int32_t* order;  // [batch, h_kv, max_nq, kmax] (null for dense)
+  const int32_t* count;  // [batch, h_kv, max_nq]      (null for dense)
+  int32_t* visited;      // [batch, h_q, max_nq]       (null for dense)
+  int32_t* skipped;      // [batch, h_q, max_nq]       (null for dense)
+  uint8_t* skip_bits;    // [batch, h_q, max_nq, kmax] (nullable)
+  float* lse;            // [h_q, total_q]             (nullable)
+  int32_t total_q;
+  int32_t kmax;
+  float scale;           // softmax scale
+  float scale_log2;      // softmax scale * log2(e)
+  float skip_thr_raw;    // ln(tau) / scale: threshold on raw q.k differences
+  int32_t skip_on;       // tau > 0
+  int64_t n_units;       // batch * h_q * max_nq
+};
+
+// Proxy launches.
+struct KapArgs {
+  SeqArgs seq;
+  const void* q;
+  const void* k;
+  void* q_pool;          // [batch, max_nr, h_q, d]   (dtype)
+  void* k_pool;          // [num_pages, h_kv, B/p, d] (dtype)
+  float* scores;         // P: [batch, h_q, max_nr, max_nk] fp32
+  int32_t fill_scores;   // 1: write -inf into every non-visible entry of P
+  float* block_scores;   // nullable [batch, h_kv, max_nq, max_nk]
+  int32_t* order;        // [batch, h_kv, max_nq, kmax]
+  uint8_t* hrm;          // [batch, h_kv, max_nq, kmax]
+  int32_t* count;        // [batch, h_kv, max_nq]
+  int32_t pool;
+  int32_t max_nr;
+  int32_t kmax;
+  double budget;
+  float scale;
+};
+
+// Each launcher returns hipSuccess or the launch error. `dtype` is cosa_dtype.
+hipError_t launch_osk(const OskArgs& a, int dtype, int head_dim, int block, bool dense,
+                      hipStream_t stream);
+hipError_t launch_kap(const KapArgs& a, int dtype, int head_dim, int block, hipStream_t stream);
+
+}  // namespace cosa

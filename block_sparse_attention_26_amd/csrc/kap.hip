@@ -1,0 +1,437 @@
+// Kernel-Aware Proxy (KAP) for gfx950.
+//
+// Method: CoSA technical summary (gist.science, "CoSA: Accelerating
+// Long-Context Inference via Proxy-Kernel Co-Designed Sparse Attention"),
+// §2.2 Stage 1, in the page's order:
+//   block ranking - downsample Q and K (kap_pool_q / kap_pool_k: mean over p
+//       tokens), approximate scores and MaxPool over the keys of each KV block
+//       (kap_score: MFMA GEMM with the per-block max fused into its epilogue),
+//       MaxNorm (kap_rank_sort: exp(P - row max));
+//   HRM flag generation - blocks that attain some pooled row's max, united
+//       over the query heads of a KV group (the GQA union follows the
+//       CompactAttention page, selection stage);
+//   flag-grouped sorting - HRM blocks first, then by block score, cut to the
+//       row's budget (kap_rank_sort: bitonic sort of 64-bit keys in LDS).
+// §2.1 defines the result as a computation order, not a binary mask.
+//
+// Bit-exact contract: from the fp32 proxy scores P onwards every operation
+// is one IEEE binary32 operation in a fixed order (row max, P - max, exp32,
+// a sequential sum over heads then rows, exact comparisons), so order, HRM
+// flags and block scores equal those of any other IEEE implementation given
+// the same P. Floating-point contraction is disabled for that code.
+#include <math.h>
+
+#include "cosa_internal.h"
+
+namespace cosa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
+  return __builtin_bit_cast(float, h16 << 16);
+}
+
+// 8 consecutive elements -> fp32
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* base, size_t elem, float* out) {
+  if constexpr (BF16) {
+    const uint4 x = *(const uint4*)((const uint16_t*)base + elem);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+      out[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    }
+  } else {
+    const float4 x0 = *(const float4*)((const float*)base + elem);
+    const float4 x1 = *(const float4*)((const float*)base + elem + 4);
+    out[0] = x0.x; out[1] = x0.y; out[2] = x0.z; out[3] = x0.w;
+    out[4] = x1.x; out[5] = x1.y; out[6] = x1.z; out[7] = x1.w;
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store8(void* base, size_t elem, const float* v) {
+  if constexpr (BF16) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2 * i]) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2 * i + 1]) << 16);
+    *(uint4*)((uint16_t*)base + elem) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    *(float4*)((float*)base + elem) = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)((float*)base + elem + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+// ---- pooling (reading R1: mean over p consecutive tokens) ------------------
+// One workgroup per (sequence, pooled row); 8-element chunks over h_q * D.
+template <bool BF16, int D>
+__global__ __launch_bounds__(kThreads) void kap_pool_q(KapArgs a) {
+  const SeqArgs& sq = a.seq;
+  const int b = blockIdx.x / a.max_nr, r = blockIdx.x % a.max_nr;
+  const int q0 = sq.cu_seqlens_q[b];
+  const int Lq = sq.cu_seqlens_q[b + 1] - q0;
+  const int lo = r * a.pool;
+  if (lo >= Lq) return;
+  const int hi = min(lo + a.pool, Lq);
+  const float inv_cnt = 1.f / (float)(hi - lo);
+  const int chunks = sq.h_q * D / 8;
+  for (int c = threadIdx.x; c < chunks; c += kThreads) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int tok = lo; tok < hi; ++tok) {
+      float x[8];
+      load8<BF16>(a.q, (size_t)(q0 + tok) * sq.h_q * D + (size_t)c * 8, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += x[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= inv_cnt;
+    store8<BF16>(a.q_pool, ((size_t)b * a.max_nr + r) * sq.h_q * D + (size_t)c * 8, acc);
+  }
+}
+
+// One workgroup per (sequence, KV block): pools the page into B/p slots.
+template <bool BF16, int D, int BLK>
+__global__ __launch_bounds__(kThreads) void kap_pool_k(KapArgs a) {
+  const SeqArgs& sq = a.seq;
+  const int b = blockIdx.x / sq.max_nk, kb = blockIdx.x % sq.max_nk;
+  const int Lk = sq.seqlens_k[b];
+  if (kb * BLK >= Lk) return;
+  const int page = sq.block_table[(int64_t)b * sq.max_blocks_k + kb];
+  if ((unsigned)page >= (unsigned)sq.num_pages) return;
+  const int nvalid = min(BLK, Lk - kb * BLK);
+  const int per = BLK / a.pool;  // pooled slots per page
+  constexpr int CH = D / 8;
+  const int chunks = sq.h_kv * per * CH;
+  for (int c = threadIdx.x; c < chunks; c += kThreads) {
+    const int dch = c % CH;
+    const int slot = (c / CH) % per;
+    const int g = c / (CH * per);
+    const int lo = slot * a.pool;
+    const int hi = min(lo + a.pool, nvalid);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int tok = lo; tok < hi; ++tok) {
+      float x[8];
+      load8<BF16>(a.k, (((size_t)page * sq.h_kv + g) * BLK + tok) * D + dch * 8, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += x[i];
+    }
+    const float inv_cnt = hi > lo ? 1.f / (float)(hi - lo) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= inv_cnt;
+    store8<BF16>(a.k_pool, (((size_t)page * sq.h_kv + g) * per + slot) * D + dch * 8, acc);
+  }
+}
+
+// ---- proxy scores with fused MaxPool (readings R2-R4) ----------------------
+// One workgroup per (sequence, query head, tile of 32 pooled rows), longest
+// tiles first. Each of the 4 waves computes a 32-key x 32-row tile of
+// S^T = Kpool . Qpool^T per step (128 pooled keys per step); the tile goes
+// through LDS and the workgroup reduces it to per-KV-block maxima.
+constexpr int kScoreRows = 32;
+constexpr int kScoreKeys = 128;
+
+template <bool BF16, int D, int BLK>
+__global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
+  __shared__ float tile[kScoreRows][kScoreKeys + 1];
+  const SeqArgs& sq = a.seq;
+  const int G = sq.group;
+  const int ntile = (a.max_nr + kScoreRows - 1) / kScoreRows;
+  const int64_t bid = blockIdx.x;
+  const int h = (int)(bid % sq.h_q);
+  int64_t rest = bid / sq.h_q;
+  const int b = (int)(rest % sq.batch);
+  const int rt = ntile - 1 - (int)(rest / sq.batch);
+  const int g = h / G;
+  const int q0 = sq.cu_seqlens_q[b];
+  const int Lq = sq.cu_seqlens_q[b + 1] - q0;
+  const int Lk = sq.seqlens_k[b];
+  const int off = Lk - Lq;
+  const int p = a.pool;
+  const int per = BLK / p;  // pooled keys per KV block
+  const int R = (Lq + p - 1) / p;
+  const int Rk = (Lk + p - 1) / p;
+  const int nk = (Lk + BLK - 1) / BLK;
+  const int r0 = rt * kScoreRows;
+  float* P = a.scores + (((int64_t)b * sq.h_q + h) * a.max_nr) * sq.max_nk;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hl = lane >> 5;
+
+  if (r0 >= R) {
+    if (a.fill_scores)
+      for (int i = tid; i < kScoreRows * sq.max_nk; i += kThreads) {
+        const int r = r0 + i / sq.max_nk;
+        if (r < a.max_nr) P[(int64_t)r * sq.max_nk + i % sq.max_nk] = kNegInf;
+      }
+    return;
+  }
+  // Blocks computed: every causal block of the query block holding the
+  // tile's last row (a superset of what any row of the tile can see).
+  const int r_last = min(r0 + kScoreRows, R) - 1;
+  const int qb_last = r_last / per;
+  const int kb_end = min((off + min(qb_last * BLK + BLK - 1, Lq - 1)) / BLK + 1, nk);
+
+  // this lane's query row (B operand)
+  const int my_r = r0 + l32;
+  const bool r_ok = my_r < R;
+  const int my_jmax = r_ok ? (off + min(my_r * p + p - 1, Lq - 1)) / p : -1;
+  constexpr int QREGS = BF16 ? D / 16 : D / 2;
+  bf16x8 qf16[BF16 ? QREGS : 1];
+  float qf32[BF16 ? 1 : QREGS];
+  {
+    const size_t qoff = (((size_t)b * a.max_nr + (r_ok ? my_r : r0)) * sq.h_q + h) * D;
+    if constexpr (BF16) {
+      const uint16_t* qp = (const uint16_t*)a.q_pool + qoff + hl * 8;
+#pragma unroll
+      for (int ks = 0; ks < QREGS; ++ks) {
+        uint4 x = r_ok ? *(const uint4*)(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+        qf16[ks] = __builtin_bit_cast(bf16x8, x);
+      }
+    } else {
+      const float* qp = (const float*)a.q_pool + qoff + hl;
+#pragma unroll
+      for (int ks = 0; ks < QREGS; ++ks) qf32[ks] = r_ok ? qp[2 * ks] : 0.f;
+    }
+  }
+
+  const int jend = kb_end * per;  // pooled keys covered
+  for (int j0 = 0; j0 < jend; j0 += kScoreKeys) {
+    // ---- one 32x32 MFMA tile per wave: keys j0 + w*32 + [0,32) ----------
+    const int jk = j0 + w * 32 + l32;  // the key row this lane loads (A operand)
+    const bool k_ok = jk < Rk && jk < jend;
+    size_t koff = 0;
+    if (k_ok) {
+      const int kbk = jk / per;
+      const int page = sq.block_table[(int64_t)b * sq.max_blocks_k + kbk];
+      koff = ((((size_t)page * sq.h_kv + g) * per) + jk % per) * D;
+    }
+    f32x16 s;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = 0.f;
+    if constexpr (BF16) {
+      const uint16_t* kp = (const uint16_t*)a.k_pool + koff + hl * 8;
+#pragma unroll
+      for (int ks = 0; ks < QREGS; ++ks) {
+        uint4 x = k_ok ? *(const uint4*)(kp + ks * 16) : make_uint4(0, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), qf16[ks], s, 0, 0, 0);
+      }
+    } else {
+      const float* kp = (const float*)a.k_pool + koff + hl;
+#pragma unroll
+      for (int ks = 0; ks < QREGS; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(k_ok ? kp[2 * ks] : 0.f, qf32[ks], s, 0, 0, 0);
+    }
+    __syncthreads();  // previous step's tile fully consumed
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int jj = w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3);  // key within the step
+      const int j = j0 + jj;
+      const float x = (j <= my_jmax && j < Rk) ? s[v] * a.scale : kNegInf;
+      tile[l32][jj] = x;
+    }
+    __syncthreads();
+    // ---- per-block maxima of the 128-key step ------------------------------
+    const int nblk = kScoreKeys / per < 1 ? 1 : kScoreKeys / per;
+    for (int i = tid; i < kScoreRows * nblk; i += kThreads) {
+      const int rr = i / nblk, bi = i % nblk;
+      const int kb = (j0 + bi * per) / per;
+      const int r = r0 + rr;
+      if (r >= R || kb >= kb_end) continue;
+      float m = kNegInf;
+      for (int e = 0; e < per; ++e) m = fmaxf(m, tile[rr][bi * per + e]);
+      P[(int64_t)r * sq.max_nk + kb] = m;
+    }
+  }
+  if (a.fill_scores) {
+    // -inf for blocks past this tile's reach and for padding rows
+    for (int i = tid; i < kScoreRows * sq.max_nk; i += kThreads) {
+      const int r = r0 + i / sq.max_nk, kb = i % sq.max_nk;
+      if (r >= a.max_nr) continue;
+      if (r >= R || kb >= kb_end) P[(int64_t)r * sq.max_nk + kb] = kNegInf;
+    }
+  }
+}
+
+// ---- exp32: the proxy's exponential, as specified ---------------------------
+// 0 unless x >= -87; t = x*fp32(log2 e); n = rint(t); f = t - n;
+// Horner over c_k = fp32(ln2^k / k!), k = 7..0; result p * 2^n.
+__device__ float exp32(float x) {
+#pragma clang fp contract(off)
+  if (!(x >= -87.0f)) return 0.0f;
+  const float t = x * __builtin_bit_cast(float, 0x3FB8AA3Bu);
+  const float n = __builtin_rintf(t);
+  const float f = t - n;
+  float p = __builtin_bit_cast(float, 0x377FE5FEu);            // ln2^7/7!
+  p = f * p; p = p + __builtin_bit_cast(float, 0x39218489u);   // ln2^6/6!
+  p = f * p; p = p + __builtin_bit_cast(float, 0x3AAEC3FFu);   // ln2^5/5!
+  p = f * p; p = p + __builtin_bit_cast(float, 0x3C1D955Bu);   // ln2^4/4!
+  p = f * p; p = p + __builtin_bit_cast(float, 0x3D635847u);   // ln2^3/3!
+  p = f * p; p = p + __builtin_bit_cast(float, 0x3E75FDF0u);   // ln2^2/2!
+  p = f * p; p = p + __builtin_bit_cast(float, 0x3F317218u);   // ln2
+  p = f * p; p = p + 1.0f;
+  return __builtin_ldexpf(p, (int)n);
+}
+
+// ---- MaxNorm, HRM, block score, flag-grouped sort, budget (R5-R10) ---------
+// One workgroup per (sequence, KV group, query block), longest rows first.
+constexpr int kMaxRankRows = 4096;  // G * (B/p) pooled rows per list
+
+template <int BLK>
+__global__ __launch_bounds__(kThreads) void kap_rank_sort(KapArgs a) {
+  __shared__ unsigned long long keys[kMaxSortBlocks];
+  __shared__ float rmax[kMaxRankRows];
+  const SeqArgs& sq = a.seq;
+  const int G = sq.group;
+  const int64_t bid = blockIdx.x;
+  const int g = (int)(bid % sq.h_kv);
+  int64_t rest = bid / sq.h_kv;
+  const int b = (int)(rest % sq.batch);
+  const int qb = sq.max_nq - 1 - (int)(rest / sq.batch);
+  const int q0 = sq.cu_seqlens_q[b];
+  const int Lq = sq.cu_seqlens_q[b + 1] - q0;
+  const int Lk = sq.seqlens_k[b];
+  const int off = Lk - Lq;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t list_row = ((int64_t)b * sq.h_kv + g) * sq.max_nq + qb;
+  int32_t* order = a.order + list_row * a.kmax;
+  uint8_t* hrm = a.hrm + list_row * a.kmax;
+  float* bs = a.block_scores ? a.block_scores + list_row * sq.max_nk : nullptr;
+
+  if (qb * BLK >= Lq) {  // past this sequence's end: empty list
+    for (int t = tid; t < a.kmax; t += kThreads) {
+      order[t] = -1;
+      hrm[t] = 0;
+    }
+    if (bs)
+      for (int kb = tid; kb < sq.max_nk; kb += kThreads) bs[kb] = 0.f;
+    if (tid == 0) a.count[list_row] = 0;
+    return;
+  }
+  const int n = (off + min(qb * BLK + BLK - 1, Lq - 1)) / BLK + 1;
+  const int p = a.pool, per = BLK / p;
+  const int R = (Lq + p - 1) / p;
+  const int r0 = qb * per;
+  const int nrow = min(r0 + per, R) - r0;
+  const int NR = G * nrow;
+  const float* Pb = a.scores + ((int64_t)b * sq.h_q) * a.max_nr * sq.max_nk;
+
+  // row maxima over the row's causal blocks (max is exact in any order)
+  for (int ri = w; ri < NR; ri += kThreads / 64) {
+    const int h = g * G + ri / nrow, r = r0 + ri % nrow;
+    const float* row = Pb + ((int64_t)h * a.max_nr + r) * sq.max_nk;
+    float m = kNegInf;
+    for (int kb = lane; kb < n; kb += 64) m = fmaxf(m, row[kb]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) rmax[ri] = m;
+  }
+  __syncthreads();
+
+  int npad = 1;
+  while (npad < n) npad <<= 1;
+  for (int kb = tid; kb < npad; kb += kThreads) {
+    unsigned long long key = 0ull;
+    if (kb < n) {
+      float s = 0.0f;
+      bool flag = false;
+      for (int ri = 0; ri < NR; ++ri) {  // heads ascending, then rows ascending
+        const int h = g * G + ri / nrow, r = r0 + ri % nrow;
+        const float x = Pb[((int64_t)h * a.max_nr + r) * sq.max_nk + kb];
+        float dlt;
+        {
+#pragma clang fp contract(off)
+          dlt = x - rmax[ri];
+          s = s + exp32(dlt);
+        }
+        flag |= (dlt == 0.0f);
+      }
+      key = ((unsigned long long)(flag ? 1u : 0u) << 63) |
+            ((unsigned long long)__builtin_bit_cast(uint32_t, s) << 32) |
+            (unsigned long long)(0xFFFFFFFFu - (uint32_t)kb);
+      if (bs) bs[kb] = s;
+    }
+    keys[kb] = key;
+  }
+  if (bs)
+    for (int kb = n + tid; kb < sq.max_nk; kb += kThreads) bs[kb] = 0.f;
+  __syncthreads();
+
+  // bitonic sort, descending
+  for (int k = 2; k <= npad; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < npad; i += kThreads) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const unsigned long long x = keys[i], y = keys[ixj];
+          const bool desc = (i & k) == 0;
+          if (desc ? (x < y) : (x > y)) {
+            keys[i] = y;
+            keys[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  int kcnt = (int)ceil(a.budget * (double)n - 1e-9);
+  kcnt = max(1, min(n, kcnt));
+  for (int t = tid; t < a.kmax; t += kThreads) {
+    if (t < kcnt) {
+      const unsigned long long key = keys[t];
+      order[t] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
+      hrm[t] = (uint8_t)(key >> 63);
+    } else {
+      order[t] = -1;
+      hrm[t] = 0;
+    }
+  }
+  if (tid == 0) a.count[list_row] = kcnt;
+}
+
+template <bool BF16, int D, int BLK>
+hipError_t launch_all(const KapArgs& a, hipStream_t stream) {
+  const SeqArgs& sq = a.seq;
+  const int64_t g1 = (int64_t)sq.batch * a.max_nr;
+  hipLaunchKernelGGL((kap_pool_q<BF16, D>), dim3((unsigned)g1), dim3(kThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t g2 = (int64_t)sq.batch * sq.max_nk;
+  hipLaunchKernelGGL((kap_pool_k<BF16, D, BLK>), dim3((unsigned)g2), dim3(kThreads), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t ntile = (a.max_nr + kScoreRows - 1) / kScoreRows;
+  const int64_t g3 = ntile * sq.batch * sq.h_q;
+  hipLaunchKernelGGL((kap_score<BF16, D, BLK>), dim3((unsigned)g3), dim3(kThreads), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t g4 = (int64_t)sq.max_nq * sq.batch * sq.h_kv;
+  hipLaunchKernelGGL((kap_rank_sort<BLK>), dim3((unsigned)g4), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_kap(const KapArgs& a, int dtype, int head_dim, int block, hipStream_t stream) {
+  const bool bf = dtype == 1;
+#define COSA_KAP_CASE(BF, DD, BB) \
+  if (bf == BF && head_dim == DD && block == BB) return launch_all<BF, DD, BB>(a, stream);
+  COSA_KAP_CASE(true, 128, 128)
+  COSA_KAP_CASE(true, 128, 64)
+  COSA_KAP_CASE(true, 64, 128)
+  COSA_KAP_CASE(true, 64, 64)
+  COSA_KAP_CASE(false, 128, 128)
+  COSA_KAP_CASE(false, 128, 64)
+  COSA_KAP_CASE(false, 64, 128)
+  COSA_KAP_CASE(false, 64, 64)
+#undef COSA_KAP_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace cosa

@@ -1,0 +1,210 @@
+/*
+ * cosa.h - C ABI of libcosa: CoSA block-sparse causal prefill attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one summarised on the gist.science pages "CoSA:
+ * Accelerating Long-Context Inference via Proxy-Kernel Co-Designed Sparse
+ * Attention" (technical summary). Stage 1, the Kernel-Aware Proxy (KAP, §2.2),
+ * turns downsampled query/key scores into a per-query-block computation-order
+ * list; stage 2, the Ordered-Skipping Kernel (OSK, §2.3), runs online-softmax
+ * attention over the listed KV pages in that order and skips, in-kernel,
+ * blocks whose local maxima sit far below the running maxima.
+ *
+ * General rules for every entry point:
+ *  - Pointers named in a cosa_problem and every tensor argument are DEVICE
+ *    pointers unless the name starts with "host_". The caller owns all
+ *    memory; the library allocates nothing and keeps no pointer after return.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    returns without synchronising. No device-to-host copy is made.
+ *  - Arguments are validated on the host before any HIP call. A rejected call
+ *    returns COSA_ERR_INVALID_ARG or COSA_ERR_UNSUPPORTED and enqueues
+ *    nothing; cosa_last_error() then names the offending argument. A failed
+ *    kernel launch returns COSA_ERR_HIP.
+ *  - Results are deterministic: the same inputs give bitwise-identical
+ *    outputs from run to run (no atomics in any accumulation).
+ *  - Calls are reentrant; the error message is thread-local.
+ *
+ * Layouts (element counts, row-major, all contiguous):
+ *  q, o        [total_q, h_q, head_dim]   sequences packed back to back;
+ *              sequence b owns rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1.
+ *  k/v pages   [num_pages, h_kv, block, head_dim]: KV-head-major pages, one
+ *              page per (logical KV block) so each (page, KV head) slab is
+ *              contiguous (layout of the CompactAttention page, execution
+ *              stage). block_table[b * max_blocks_k + kb] names the page that
+ *              holds keys kb*block .. kb*block+block-1 of sequence b. Key slots
+ *              past a sequence's end may hold anything (even NaN): they are
+ *              never used.
+ *  Causality: sequence b has Lq = cu_seqlens_q[b+1]-cu_seqlens_q[b] queries
+ *  and Lk = seqlens_k[b] >= Lq keys. Local query i sits at absolute position
+ *  off + i, off = Lk - Lq (a prefill chunk attending to the KV cache that
+ *  already holds it), and sees keys j <= off + i.
+ *  Blocks: query block qb holds local rows qb*block .. qb*block+block-1; KV
+ *  block kb is causal for qb when kb*block <= off + min(qb*block+block-1,
+ *  Lq-1); the causal blocks of qb are kb = 0 .. n(qb)-1.
+ */
+#ifndef COSA_H
+#define COSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum cosa_status {
+  COSA_OK = 0,
+  COSA_ERR_INVALID_ARG = -1, /* argument out of its documented domain       */
+  COSA_ERR_UNSUPPORTED = -2, /* valid, but a size this build does not handle */
+  COSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required  */
+  COSA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed  */
+} cosa_status;
+
+typedef enum cosa_dtype { COSA_F32 = 0, COSA_BF16 = 1 } cosa_dtype;
+
+/* Shape and metadata of one packed prefill batch. */
+typedef struct cosa_problem {
+  int32_t batch;       /* number of sequences, >= 1                          */
+  int32_t h_q;         /* query heads, >= 1                                  */
+  int32_t h_kv;        /* KV heads, >= 1, divides h_q (GQA group G=h_q/h_kv) */
+  int32_t head_dim;    /* 64 or 128                                          */
+  int32_t block;       /* B: query-block rows = KV-block keys = page size;
+                          64 or 128                                          */
+  int32_t dtype;       /* cosa_dtype of q, k/v pages and o                   */
+  float softmax_scale; /* > 0, usually 1/sqrt(head_dim)                      */
+  int32_t num_pages;   /* pages in the k/v pools                             */
+  int32_t max_blocks_k;/* row length of block_table (>= ceil(Lk/B) for all b)*/
+  const int32_t* cu_seqlens_q;      /* device [batch+1], cu[0]=0, nondecreasing */
+  const int32_t* seqlens_k;         /* device [batch]                          */
+  const int32_t* block_table;       /* device [batch, max_blocks_k], entries
+                                       in [0, num_pages)                       */
+  const int32_t* host_cu_seqlens_q; /* host copy of cu_seqlens_q              */
+  const int32_t* host_seqlens_k;    /* host copy of seqlens_k                  */
+} cosa_problem;
+
+/* Padded extents derived from a problem (see cosa_dims). */
+typedef struct cosa_dims_t {
+  int32_t total_q; /* cu_seqlens_q[batch]                                   */
+  int32_t max_nq;  /* max_b ceil(Lq_b / B): query blocks per sequence (padded)*/
+  int32_t max_nk;  /* max_b ceil(Lk_b / B): KV blocks per sequence (padded)    */
+  int32_t max_nr;  /* max_b ceil(Lq_b / pool): pooled query rows (padded)      */
+  int32_t kmax;    /* widest order list under `budget` (closed form, >= 1)     */
+} cosa_dims_t;
+
+/* Host-only check of a problem (no HIP call, usable without a GPU).
+ * Returns COSA_OK or the reason it was rejected. */
+cosa_status cosa_validate(const cosa_problem* problem);
+
+/* Host-only: padded extents for this problem, pool factor and budget.
+ * kmax = max over rows of k(qb) = clamp(ceil(budget*n(qb) - 1e-9), 1, n(qb)),
+ * evaluated in IEEE double (the budget rule of the CoSA summary §2.2, read
+ * as a per-row fraction of the causal blocks). pool may be 0 when only the
+ * attention extents are needed (max_nr is then 0); budget may be 0 for the
+ * same purpose (kmax is then 0). */
+cosa_status cosa_dims(const cosa_problem* problem, int32_t pool, double budget,
+                      cosa_dims_t* out /* host */);
+
+/* Bytes of device workspace cosa_kap_order needs; `with_scores` = 0 when the
+ * caller passes its own proxy_scores buffer (the scores then live there).
+ * Returns 0 for an invalid problem or pool. */
+size_t cosa_kap_workspace_size(const cosa_problem* problem, int32_t pool, int32_t with_scores);
+
+/* Stage 1, Kernel-Aware Proxy (CoSA summary §2.2: block ranking, HRM flag
+ * generation, flag-grouped sorting; §2.1: the output prescribes an order).
+ *
+ *  pool    p: tokens per pooled vector, 1 <= p <= B and p divides B. Q and K
+ *          are mean-pooled over p consecutive tokens (a ragged last window
+ *          averages the tokens that exist).
+ *  budget  beta in (0, 1]: each row keeps k(qb) of its n(qb) causal blocks.
+ *  Proxy scores: P[b,h,r,kb] = max over the pooled keys j of block kb that
+ *          pooled row r may see (j*p <= off + min(r*p+p-1, Lq-1)) of
+ *          softmax_scale * qpool[r,h] . kpool[j, h/G]; -inf when none.
+ *  MaxNorm: c = exp32(P - rowmax(P)) (fp32, see below).
+ *  HRM:    block kb is flagged for (b, g, qb) when P[b,h,r,kb] equals the
+ *          row max for some pooled row r of qb and some query head h of KV
+ *          group g.
+ *  Score:  s[b,g,qb,kb] = sum of c over the group's heads (ascending), then
+ *          qb's pooled rows (ascending), one rounded fp32 add at a time.
+ *  Order:  the causal blocks of the row sorted by (HRM first, s descending,
+ *          kb ascending), truncated to the first k(qb).
+ *  exp32(x): 0 unless x >= -87; t = x*fp32(log2 e); n = rint(t) (ties even);
+ *          f = t-n; Horner p = c7, p = f*p + c_k (k=6..0) with
+ *          c_k = fp32(ln2^k/k!); result p*2^n. Every * and + is one fp32
+ *          operation, never fused. Given the same fp32 P, order, hrm and s
+ *          are reproducible bit for bit on any IEEE machine.
+ *
+ * Outputs (device):
+ *  order        int32 [batch, h_kv, max_nq, kmax]: listed KV blocks, -1 pad.
+ *  hrm          uint8 [batch, h_kv, max_nq, kmax]: 1 where the listed block
+ *               is an HRM block, 0 otherwise and in the padding.
+ *  count        int32 [batch, h_kv, max_nq]: k(qb); 0 for qb past a
+ *               sequence's last query block.
+ *  kmax         the caller's list width; must be >= cosa_dims().kmax.
+ *  proxy_scores nullable fp32 [batch, h_q, max_nr, max_nk]: P, with -inf in
+ *               every padding or non-visible entry.
+ *  block_scores nullable fp32 [batch, h_kv, max_nq, max_nk]: s for
+ *               kb < n(qb), 0 elsewhere.
+ *  workspace    device scratch of cosa_kap_workspace_size(problem, pool,
+ *               proxy_scores == NULL) bytes, 256-byte aligned; its contents
+ *               on entry do not matter.
+ * Limits: max_nk <= 4096 (COSA_ERR_UNSUPPORTED beyond). */
+cosa_status cosa_kap_order(const cosa_problem* problem, const void* q, const void* k_pages,
+                           int32_t pool, double budget, int32_t* order, uint8_t* hrm,
+                           int32_t* count, int32_t kmax, float* proxy_scores,
+                           float* block_scores, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Stage 2, Ordered-Skipping Kernel (CoSA summary §2.3: mask-skipped pages are
+ * never touched, retained blocks may be skipped in-kernel, the rest is
+ * computed; §1 for the per-tile veto).
+ *
+ * For each (b, query head h, qb) the kernel walks t = 0 .. count[b,g,qb]-1
+ * over the list of KV group g = h / group, gathers page
+ * block_table[b, order[b,g,qb,t]] in place and computes the scaled scores of
+ * all valid rows of qb against its visible keys. With skip_threshold tau in
+ * (0, 1) the block is skipped when, for every valid row i with a visible key
+ * in it, m_loc_i - m_i < ln(tau) (m_loc_i its max scaled score in the block,
+ * m_i the running max before the block, -inf before any block); a skipped
+ * block leaves the running max, sum and accumulator unchanged. Otherwise the
+ * online-softmax update runs and the P.V product is accumulated. tau = 0
+ * never skips. O = acc / sum per row (0 for a row that saw no key).
+ *
+ *  order, count  as written by cosa_kap_order (any list of distinct causal
+ *                blocks is accepted; an entry that is not a causal block of
+ *                its row makes that row's output NaN).
+ *  group         must equal h_q / h_kv.
+ *  o             [total_q, h_q, head_dim] in the problem's dtype.
+ *  visited       int32 [batch, h_q, max_nq]: listed blocks walked (= count).
+ *  skipped       int32 [batch, h_q, max_nq]: blocks skipped in-kernel.
+ *  skip_bits     nullable uint8 [batch, h_q, max_nq, kmax]: 0 computed,
+ *                1 skipped, 255 padding.
+ *  lse           nullable fp32 [h_q, total_q]: natural-log sum-exp of the
+ *                computed scores of each row (-inf for a row that saw none).
+ * For qb past a sequence's end, visited and skipped are 0 and skip_bits 255. */
+cosa_status cosa_osk_attention(const cosa_problem* problem, const void* q, const void* k_pages,
+                               const void* v_pages, const int32_t* order, const int32_t* count,
+                               int32_t kmax, int32_t group, float skip_threshold, void* o,
+                               int32_t* visited, int32_t* skipped, uint8_t* skip_bits, float* lse,
+                               void* stream);
+
+/* Dense causal softmax attention, the baseline of the CoSA summary §4: the
+ * same tile engine walking every causal block of each row in ascending order,
+ * with no list and no skip test. o and lse as in cosa_osk_attention. */
+cosa_status cosa_dense_attention(const cosa_problem* problem, const void* q, const void* k_pages,
+                                 const void* v_pages, void* o, float* lse, void* stream);
+
+/* Static description of a status code. */
+const char* cosa_status_string(cosa_status status);
+
+/* Thread-local message of the last rejected or failed call on this thread
+ * ("" after a successful call). */
+const char* cosa_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t cosa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COSA_H */

@@ -5,7 +5,7 @@ exactly to fp64. Outputs use the same shapes the C-ABI writes:
 
     order, hrm      [batch, h_kv, max_nq, kmax]   (int32 -1 pad, uint8 0 pad)
     count           [batch, h_kv, max_nq]
-    P               [h_q, batch, max_nr, max_nk]  (fp32 or fp64, -inf pad)
+    P               [batch, h_q, max_nr, max_nk]  (fp32 or fp64, -inf pad)
     s               [batch, h_kv, max_nq, max_nk] (block scores, 0 pad)
     O               [total_q, h_q, d]
     lse             [h_q, total_q]
@@ -50,7 +50,7 @@ def dims(case):
 
 
 def kap_case(case, precision: str = "fp64", P_given=None, budget=None):
-    """The proxy over the batch. With ``P_given`` ([h_q, batch, max_nr, max_nk]
+    """The proxy over the batch. With ``P_given`` ([batch, h_q, max_nr, max_nk]
     fp32, e.g. the GPU's exported scores) only the ranking, flagging and sort
     run (parity mode)."""
     dm = dims(case)
@@ -63,7 +63,7 @@ def kap_case(case, precision: str = "fp64", P_given=None, budget=None):
     order = np.full((nb, Hkv, dm["max_nq"], kmax), -1, dtype=np.int32)
     hrm = np.zeros((nb, Hkv, dm["max_nq"], kmax), dtype=np.uint8)
     count = np.zeros((nb, Hkv, dm["max_nq"]), dtype=np.int32)
-    P = np.full((Hq, nb, dm["max_nr"], dm["max_nk"]), -np.inf, dtype=fdt)
+    P = np.full((nb, Hq, dm["max_nr"], dm["max_nk"]), -np.inf, dtype=fdt)
     s = np.zeros((nb, Hkv, dm["max_nq"], dm["max_nk"]), dtype=fdt)
     for b in range(nb):
         Lq = case.seqlens_q[b]
@@ -72,7 +72,7 @@ def kap_case(case, precision: str = "fp64", P_given=None, budget=None):
             continue
         nq, nk, nr = cdiv(Lq, B), cdiv(Lk, B), cdiv(Lq, p)
         if P_given is not None:
-            Pb = np.asarray(P_given[:, b, :nr, :nk])
+            Pb = np.asarray(P_given[b, :, :nr, :nk])
             out = _kap.kap_from_scores(Pb, Hq // Hkv, B, p, Lq, Lk, budget, kmax, precision)
             out["P"] = Pb
         else:
@@ -81,7 +81,7 @@ def kap_case(case, precision: str = "fp64", P_given=None, budget=None):
         order[b, :, :nq] = out["order"]
         hrm[b, :, :nq] = out["hrm"]
         count[b, :, :nq] = out["count"]
-        P[:, b, :nr, :nk] = out["P"]
+        P[b, :, :nr, :nk] = out["P"]
         s[b, :, :nq, :nk] = out["s"]
     return {"order": order, "hrm": hrm, "count": count, "P": P, "s": s, "kmax": kmax}
 

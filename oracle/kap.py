@@ -80,42 +80,63 @@ def proxy_scores(qt, kt, scale: float, B: int, p: int, Lq: int, Lk: int) -> np.n
     return P
 
 
-def rank(P, G: int, B: int, p: int, Lq: int, precision: str = "fp32"):
-    """R5-R8: MaxNorm contributions, HRM flags and per-block scores.
+def rank_row(P_rows, precision: str = "fp32"):
+    """R5-R7 for one list row (b, g, qb).
 
-    P [Hq, R, Nk]. Returns (s, hrm) with shapes [Hkv, Nq, Nk]."""
-    if precision == "fp32":
-        P = np.asarray(P, dtype=np.float32)
-    else:
-        P = np.asarray(P, dtype=np.float64)
-    Hq, R, Nk = P.shape
-    Hkv = Hq // G
-    Nq = cdiv(Lq, B)
-    per = B // p
+    P_rows [G, nrow, nk]: the proxy scores of the group's query heads
+    (ascending) for the pooled rows of qb (ascending), over the sequence's KV
+    blocks. Returns (s [nk], hrm [nk])."""
+    dt = np.float32 if precision == "fp32" else np.float64
+    P_rows = np.asarray(P_rows, dtype=dt)
     with np.errstate(invalid="ignore"):
-        m = P.max(axis=2, keepdims=True)  # row max (exact in any precision)
-        D = (P - m).astype(P.dtype)
+        m = P_rows.max(axis=2, keepdims=True)  # row max (exact in any precision)
+        D = (P_rows - m).astype(dt)
         if precision == "fp32":
             c = exp32(D)
         else:
-            c = np.where(D >= -np.inf, np.exp(D), 0.0)  # NaN -> 0
-            c = np.nan_to_num(c, nan=0.0)
+            c = np.nan_to_num(np.exp(D), nan=0.0)  # exp(-inf) = 0, NaN -> 0
     flag = D == 0
-    s = np.zeros((Hkv, Nq, Nk), dtype=P.dtype)
+    nk = P_rows.shape[2]
+    s = np.zeros(nk, dtype=dt)
+    hrm = np.zeros(nk, dtype=bool)
+    for h in range(P_rows.shape[0]):
+        for r in range(P_rows.shape[1]):
+            s = (s + c[h, r]).astype(dt)  # one rounded add per term, per block
+            hrm |= flag[h, r]
+    return s, hrm
+
+
+def select_row(s, hrm, n: int, budget: float):
+    """R9-R10 for one list row: sort the n causal blocks, keep k of them.
+    Returns (order list, HRM flags of the listed blocks)."""
+    ranked = sorted(range(n), key=lambda kb: (not hrm[kb], -s[kb], kb))
+    k = budget_count(n, budget)
+    return ranked[:k], [1 if hrm[kb] else 0 for kb in ranked[:k]]
+
+
+def row_inputs(P, G: int, g: int, qb: int, B: int, p: int):
+    """The slice of P [Hq, R, Nk] that list row (g, qb) ranks."""
+    per = B // p
+    R = P.shape[1]
+    return P[g * G : (g + 1) * G, qb * per : min(qb * per + per, R), :]
+
+
+def rank(P, G: int, B: int, p: int, Lq: int, precision: str = "fp32"):
+    """R5-R8 over a whole sequence. P [Hq, R, Nk] -> (s, hrm) [Hkv, Nq, Nk]."""
+    dt = np.float32 if precision == "fp32" else np.float64
+    Hq, R, Nk = P.shape
+    Hkv = Hq // G
+    Nq = cdiv(Lq, B)
+    s = np.zeros((Hkv, Nq, Nk), dtype=dt)
     hrm = np.zeros((Hkv, Nq, Nk), dtype=bool)
     for g in range(Hkv):
         for qb in range(Nq):
-            acc = np.zeros(Nk, dtype=P.dtype)
-            for h in range(g * G, (g + 1) * G):
-                for r in range(qb * per, min(qb * per + per, R)):
-                    acc = (acc + c[h, r]).astype(P.dtype)
-                    hrm[g, qb] |= flag[h, r]
-            s[g, qb] = acc
+            s[g, qb], hrm[g, qb] = rank_row(row_inputs(P, G, g, qb, B, p), precision)
     return s, hrm
 
 
 def select(s, hrm, B: int, Lq: int, Lk: int, budget: float, kmax: int):
-    """R9-R10: flag-grouped sort of each row's causal blocks, then truncate.
+    """R9-R10 over a whole sequence.
 
     Returns order [Hkv, Nq, kmax] int32 (-1 padded), hrm_sel [Hkv, Nq, kmax]
     uint8 and count [Hkv, Nq] int32."""
@@ -126,11 +147,10 @@ def select(s, hrm, B: int, Lq: int, Lk: int, budget: float, kmax: int):
     for g in range(Hkv):
         for qb in range(Nq):
             n = n_causal_blocks(qb, B, Lq, Lk)
-            ranked = sorted(range(n), key=lambda kb: (not hrm[g, qb, kb], -s[g, qb, kb], kb))
-            k = budget_count(n, budget)
-            order[g, qb, :k] = ranked[:k]
-            hsel[g, qb, :k] = [1 if hrm[g, qb, kb] else 0 for kb in ranked[:k]]
-            count[g, qb] = k
+            lst, flags = select_row(s[g, qb], hrm[g, qb], n, budget)
+            order[g, qb, : len(lst)] = lst
+            hsel[g, qb, : len(lst)] = flags
+            count[g, qb] = len(lst)
     return order, hsel, count
 
 

@@ -1,0 +1,134 @@
+"""GPU parity of the HIP path against the CPU oracle (through the C ABI).
+
+* KAP: order, HRM flags, counts and block scores bit-exact against the oracle
+  fed the GPU's fp32 proxy scores; the proxy scores themselves within the
+  bf16/fp32 tolerance of the oracle's fp64 scores.
+* OSK: given the same order lists, visited sets identical, in-kernel skip
+  sets identical outside a 1e-3-nat band around the threshold, O within
+  2e-2 max / 2e-3 mean (bf16) or 1e-4 (fp32) of the fp64 oracle.
+* Dense: O and lse against the fp64 dense oracle.
+Cases span several tiles, ragged tails, GQA 1/4/8, chunked offsets, shuffled
+NaN-poisoned page pools and packed ragged batches.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_26_amd as cosa
+import synthetic
+from oracle import cases as oc
+from gpu_common import OnDevice, check_output, check_skip_sets, require_gpu, say, TOL
+
+pytestmark = pytest.mark.gpu
+
+
+def _lr(name, seed, lq, lk=None, hq=8, hkv=2, d=128, B=128, p=16, budget=0.25, dtype="bf16", **kw):
+    return lambda: synthetic.lowrank_case(seed, lq, lk, h_q=hq, h_kv=hkv, head_dim=d, block=B, pool=p,
+                                          budget=budget, dtype=dtype, name=name, **kw)
+
+
+CASES = {
+    "cfg1": lambda: synthetic.config_case(1),
+    "f32-sinks": _lr("f32-sinks", 11, [1024], hq=2, hkv=1, d=64, B=64, p=8, dtype="f32", sink_logit=24.0),
+    "f32-d128": _lr("f32-d128", 12, [700], hq=4, hkv=2, d=128, B=128, p=16, dtype="f32"),
+    "bf16-gqa4-ragged": _lr("bf16-gqa4-ragged", 13, [2000], hq=8, hkv=2),
+    "bf16-sinks": _lr("bf16-sinks", 14, [3000], hq=8, hkv=2, sink_logit=24.0),
+    "bf16-chunk-paged": _lr("bf16-chunk-paged", 15, [1000], [8192], hq=8, hkv=2, budget=0.1,
+                            spare_pages=16, shuffle_pages=True),
+    "bf16-varlen-gqa8": _lr("bf16-varlen-gqa8", 16, [700, 1500, 333], [700, 1700, 1333], hq=16, hkv=2,
+                            per_sequence_seeds=True, spare_pages=3, shuffle_pages=True),
+    "bf16-d64-b128": _lr("bf16-d64-b128", 17, [1500], hq=4, hkv=1, d=64, B=128, p=8),
+    "bf16-d128-b64": _lr("bf16-d128-b64", 18, [1300], [1400], hq=4, hkv=4, d=128, B=64, p=4),
+    "bf16-d64-b64-sinks": _lr("bf16-d64-b64-sinks", 19, [1100], hq=4, hkv=2, d=64, B=64, p=64,
+                              sink_logit=26.0),
+}
+
+
+@pytest.fixture(scope="module", params=list(CASES))
+def run(request):
+    require_gpu()
+    case = CASES[request.param]()
+    say("case", request.param, "q", tuple(case.q.shape), "pages", tuple(case.k_pages.shape))
+    dev = OnDevice(case)
+    ko = oc.kap_case(case)  # oracle order (fp64 proxy) drives the OSK parity
+    order = torch.from_numpy(ko["order"]).cuda()
+    count = torch.from_numpy(ko["count"]).cuda()
+    return {"name": request.param, "case": case, "dev": dev, "ko": ko, "order": order, "count": count}
+
+
+def test_osk_parity(run):
+    case, dev = run["case"], run["dev"]
+    say(run["name"], "osk")
+    g = cosa.osk_attention(dev.problem, dev.q, dev.k, dev.v, run["order"], run["count"], case.tau,
+                           skip_bits=True, lse=True)
+    torch.cuda.synchronize()
+    ref = oc.osk_case(case, run["ko"]["order"], run["ko"]["count"])
+    check_output(g["O"], ref["O"], case.dtype, run["name"])
+    namb, nskip = check_skip_sets(g, ref, run["ko"]["count"], case.h_q // case.h_kv)
+    lse = g["lse"].cpu().numpy()
+    fin = np.isfinite(ref["lse"])
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.abs(lse[fin] - ref["lse"][fin]).max() < (1e-2 if case.dtype == "bf16" else 1e-4)
+    if "sinks" in run["name"]:
+        assert nskip > 0  # the case exercises both fates
+
+
+def test_osk_deterministic(run):
+    case, dev = run["case"], run["dev"]
+    say(run["name"], "osk twice")
+    a = cosa.osk_attention(dev.problem, dev.q, dev.k, dev.v, run["order"], run["count"], case.tau,
+                           skip_bits=True)
+    b = cosa.osk_attention(dev.problem, dev.q, dev.k, dev.v, run["order"], run["count"], case.tau,
+                           skip_bits=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a["O"].view(torch.uint8), b["O"].view(torch.uint8))
+    assert torch.equal(a["skip_bits"], b["skip_bits"])
+
+
+def test_dense_parity(run):
+    case, dev = run["case"], run["dev"]
+    say(run["name"], "dense")
+    g = cosa.dense_attention(dev.problem, dev.q, dev.k, dev.v, lse=True)
+    torch.cuda.synchronize()
+    ref = oc.dense_case(case)
+    check_output(g["O"], ref["O"], case.dtype, run["name"] + " dense")
+    lse = g["lse"].cpu().numpy()
+    assert np.abs(lse - ref["lse"]).max() < (1e-2 if case.dtype == "bf16" else 1e-4)
+
+
+def test_full_budget_no_skip_equals_dense(run):
+    """Budget 1 with skipping off lists every causal block: equals dense."""
+    case, dev = run["case"], run["dev"]
+    say(run["name"], "budget 1")
+    full = cosa.kap_order(dev.problem, dev.q, dev.k, case.pool, 1.0)
+    g = cosa.osk_attention(dev.problem, dev.q, dev.k, dev.v, full["order"], full["count"], 0.0)
+    torch.cuda.synchronize()
+    ref = oc.dense_case(case)
+    check_output(g["O"], ref["O"], case.dtype, run["name"] + " budget1")
+    assert int(g["skipped"].sum()) == 0
+
+
+def test_kap_parity(run):
+    case, dev = run["case"], run["dev"]
+    say(run["name"], "kap export")
+    k = cosa.kap_order(dev.problem, dev.q, dev.k, case.pool, case.budget, export_scores=True,
+                       export_block_scores=True)
+    say(run["name"], "kap workspace")
+    k2 = cosa.kap_order(dev.problem, dev.q, dev.k, case.pool, case.budget)
+    torch.cuda.synchronize()
+    P = k["P"].cpu().numpy()
+    ref = oc.kap_case(case, precision="fp32", P_given=P)
+    for name in ("order", "hrm", "count"):
+        got = k[name].cpu().numpy()
+        np.testing.assert_array_equal(got, ref[name], err_msg=name)
+        np.testing.assert_array_equal(k2[name].cpu().numpy(), got, err_msg=name + " (workspace mode)")
+    s = k["s"].cpu().numpy()
+    assert np.array_equal(s.view(np.uint32), ref["s"].astype(np.float32).view(np.uint32)), "block scores"
+    # proxy scores upstream of the bit-exact contract: tolerance vs fp64
+    P64 = oc.kap_case(case, precision="fp64")["P"]
+    fin = np.isfinite(P64)
+    assert np.array_equal(np.isfinite(P), fin), "visibility pattern of P"
+    rel = 1e-2 if case.dtype == "bf16" else 1e-5
+    assert np.abs(P[fin] - P64[fin]).max() <= rel * np.abs(P64[fin]).max()
