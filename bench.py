@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--dense-steps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -206,6 +208,15 @@ def main():
         torch.cuda.synchronize()
         dense_ms = a_ev.elapsed_time(b_ev) / KD
         print(f"[bench] dense {dense_ms:.3f} ms", file=sys.stderr, flush=True)
+
+    if args.calibrate_copy:
+        # a plain copy of known size: reads and writes exactly 1 GiB each
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     B, D = case.block, case.head_dim
     dense_flops = cosa.dense_causal_flops(case.seqlens_q, case.seqlens_k.tolist(), case.h_q, D)

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcosa.so")
-SOURCES = ["cosa_api.cpp", "osk.hip", "kap.hip"]
+SOURCES = ["cosa_api.cpp", "osk.hip", "osk_bf16.hip", "kap.hip"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -33,6 +33,9 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
     "-Wall",
     "-Wno-unused-function",
+    # MFMA results in arch VGPRs: the softmax works on them directly instead of
+    # copying accumulators out of AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

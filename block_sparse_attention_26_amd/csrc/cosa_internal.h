@@ -67,6 +67,7 @@ struct KapArgs {
 // Each launcher returns hipSuccess or the launch error. `dtype` is cosa_dtype.
 hipError_t launch_osk(const OskArgs& a, int dtype, int head_dim, int block, bool dense,
                       hipStream_t stream);
+hipError_t launch_osk_bf16(const OskArgs& a, int head_dim, int block, bool dense, hipStream_t stream);
 hipError_t launch_kap(const KapArgs& a, int dtype, int head_dim, int block, hipStream_t stream);
 
 }  // namespace cosa

@@ -1,4 +1,6 @@
-// Ordered-Skipping Kernel (OSK) and the dense causal baseline for gfx950.
+// Ordered-Skipping Kernel (OSK) and the dense causal baseline for gfx950:
+// the generic register-staged kernel, used for fp32 inputs (the bf16 path is
+// osk_bf16.hip).
 //
 // Method: CoSA technical summary (gist.science, "CoSA: Accelerating
 // Long-Context Inference via Proxy-Kernel Co-Designed Sparse Attention"):
@@ -73,9 +75,97 @@ __device__ __forceinline__ uint32_t pack_halves(uint32_t a, uint32_t b, bool hi_
   return __builtin_amdgcn_perm(b, a, hi_half ? 0x07060302u : 0x05040100u);
 }
 
-template <bool BF16, int D, int BLK, bool DENSE>
-__global__ __launch_bounds__(2 * BLK) void osk_kernel(OskArgs a) {  // 2*BLK == Cfg::THREADS
+// Per-thread register staging of one K or V tile (global -> registers -> LDS).
+// bf16: K as 16-byte row chunks; V as one 8-key x 8-column block per thread,
+// transposed in registers on the way into the V^T tile. fp32: both row-major.
+template <bool BF16, int D, int BLK>
+struct Stage {
   using C = Cfg<BF16, D, BLK>;
+  static constexpr int THREADS = C::THREADS;
+  static constexpr int CH = BF16 ? D / 8 : D / 4;           // 16-byte chunks per key row
+  static constexpr int KPT = BLK * CH / THREADS;            // chunks per thread (K, and fp32 V)
+  static constexpr int VBLK = BF16 ? (BLK / 8) * (D / 8) : 0;  // bf16 V: 8x8 blocks
+  static constexpr int REGS = BF16 ? (KPT > 8 ? KPT : 8) : KPT;
+  uint4 r[REGS];
+
+  __device__ __forceinline__ void load_k(const void* base, int nvalid, int tid) {
+    const uint4* g = (const uint4*)base;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = i * THREADS + tid;
+      r[i] = (c / CH) < nvalid ? g[c] : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store_k(unsigned char* k_lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = i * THREADS + tid;
+      if constexpr (BF16) {
+        *(uint4*)(k_lds + (c / CH) * C::K_PITCH + (c % CH) * 16) = r[i];
+      } else {
+        uint32_t* dst = (uint32_t*)(k_lds + (c / CH) * C::K_PITCH) + (c % CH) * 4;
+        dst[0] = r[i].x; dst[1] = r[i].y; dst[2] = r[i].z; dst[3] = r[i].w;
+      }
+    }
+  }
+  __device__ __forceinline__ void load_v(const void* base, int nvalid, int tid) {
+    if constexpr (BF16) {
+      const uint4* g = (const uint4*)base;
+      const int dch = tid % (D / 8), kg = tid / (D / 8);
+      if (tid < VBLK) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int key = kg * 8 + i;
+          r[i] = key < nvalid ? g[key * (D / 8) + dch] : make_uint4(0, 0, 0, 0);
+        }
+      }
+    } else {
+      load_k(base, nvalid, tid);
+    }
+  }
+  __device__ __forceinline__ void store_v(unsigned char* v_lds, int tid) const {
+    if constexpr (BF16) {
+      const int dch = tid % (D / 8), kg = tid / (D / 8);
+      if (tid < VBLK) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          // row d = dch*8 + j of V^T: keys kg*8 .. kg*8+7
+          uint32_t o4[4];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const uint32_t lo = (&r[2 * p].x)[j / 2], hi = (&r[2 * p + 1].x)[j / 2];
+            o4[p] = pack_halves(lo, hi, j & 1);
+          }
+          unsigned char* dst = v_lds + (dch * 8 + j) * C::V_PITCH + kg * 16;
+          *(uint2*)dst = make_uint2(o4[0], o4[1]);
+          *(uint2*)(dst + 8) = make_uint2(o4[2], o4[3]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int c = i * THREADS + tid;
+        uint32_t* dst = (uint32_t*)(v_lds + (c / CH) * C::V_PITCH) + (c % CH) * 4;
+        dst[0] = r[i].x; dst[1] = r[i].y; dst[2] = r[i].z; dst[3] = r[i].w;
+      }
+    }
+  }
+};
+
+// The ordered walk. Per listed block t (K and V tiles single-buffered in LDS,
+// one staging buffer in registers cycled through three phases):
+//   barrier A  - every wave is done with PV(t-1): write V(t) from registers;
+//                start loading K(t+1) into the registers
+//   S(t) = K(t) Q^T, causal mask, row maxima, per-wave skip margin
+//   barrier C  - every wave is done reading K(t): write K(t+1) to LDS, start
+//                loading V(t+1); all margins visible -> skip decision
+//   unless skipped: online-softmax update and O^T += V(t)^T P^T
+// Two workgroups share a CU, so one's MFMA work overlaps the other's loads and
+// softmax.
+template <bool BF16, int D, int BLK, bool DENSE>
+__global__ __launch_bounds__(2 * BLK, 1) void osk_kernel(OskArgs a) {  // 2*BLK == Cfg::THREADS
+  using C = Cfg<BF16, D, BLK>;
+  using S = Stage<BF16, D, BLK>;
   __shared__ __attribute__((aligned(16))) unsigned char k_lds[C::K_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds[C::V_BYTES];
   __shared__ float red[C::NW];
@@ -111,7 +201,6 @@ __global__ __launch_bounds__(2 * BLK) void osk_kernel(OskArgs a) {  // 2*BLK == 
     return;
   }
   const int off = Lk - Lq;
-
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int l32 = lane & 31;
@@ -142,15 +231,37 @@ __global__ __launch_bounds__(2 * BLK) void osk_kernel(OskArgs a) {  // 2*BLK == 
 
   int n_list;
   const int32_t* lst = nullptr;
-  int64_t list_row = 0;
   if constexpr (DENSE) {
     n_list = n_causal;
   } else {
-    list_row = ((int64_t)b * sq.h_kv + g) * sq.max_nq + qb;
+    const int64_t list_row = ((int64_t)b * sq.h_kv + g) * sq.max_nq + qb;
     n_list = min(a.count[list_row], a.kmax);  // a corrupt count cannot overrun the row
     lst = a.order + list_row * a.kmax;
   }
   const int64_t out_row = ((int64_t)b * sq.h_q + h) * sq.max_nq + qb;
+  bool bad = false;
+  const int32_t* table = sq.block_table + (int64_t)b * sq.max_blocks_k;
+  const size_t tile_elems = (size_t)BLK * D;
+  const size_t head_off = (size_t)g * tile_elems;
+  const size_t page_elems = (size_t)sq.h_kv * tile_elems;
+  // list entry t -> (first key, element offset of its page slab for this KV head)
+  auto locate = [&](int t, int& key0, size_t& elem) {
+    int kb = DENSE ? t : lst[t];
+    if (kb < 0 || kb >= n_causal) {
+      bad = true;
+      kb = 0;
+    }
+    int page = table[kb];
+    if ((unsigned)page >= (unsigned)sq.num_pages) {
+      bad = true;
+      page = 0;
+    }
+    key0 = kb * BLK;
+    elem = (size_t)page * page_elems + head_off;
+  };
+  const unsigned char* kbase = (const unsigned char*)a.k;
+  const unsigned char* vbase = (const unsigned char*)a.v;
+  constexpr int ES = BF16 ? 2 : 4;
 
   f32x16 acc[C::DT];
 #pragma unroll
@@ -160,113 +271,52 @@ __global__ __launch_bounds__(2 * BLK) void osk_kernel(OskArgs a) {  // 2*BLK == 
   float m_run = kNegInf;  // running max of raw q.k (unscaled)
   float l_run = 0.f;      // this lane's share of the running sum
   int n_skip = 0;
-  bool bad = false;
   const float c2 = a.scale_log2;
 
-  for (int t = 0; t < n_list; ++t) {
-    int kb = DENSE ? t : lst[t];
-    if (kb < 0 || kb >= n_causal) {
-      bad = true;
-      kb = 0;
-    }
-    int page = sq.block_table[(int64_t)b * sq.max_blocks_k + kb];
-    if ((unsigned)page >= (unsigned)sq.num_pages) {
-      bad = true;
-      page = sq.block_table[(int64_t)b * sq.max_blocks_k];
-      if ((unsigned)page >= (unsigned)sq.num_pages) page = 0;
-    }
-    const int key0 = kb * BLK;
-    const int nvalid = min(BLK, Lk - key0);
+  // ---- prologue: K(0) into LDS, V(0) into the staging registers -----------
+  S stg;
+  int key0;
+  size_t elem;
+  locate(0, key0, elem);
+  stg.load_k(kbase + elem * ES, min(BLK, Lk - key0), tid);
+  stg.store_k(k_lds, tid);
+  stg.load_v(vbase + elem * ES, min(BLK, Lk - key0), tid);
 
-    // ---- gather K and V of this page into registers -----------------------
-    if constexpr (BF16) {
-      constexpr int CH = D / 8;  // 16-byte chunks per key row
-      constexpr int KPT = BLK * CH / C::THREADS;
-      constexpr int VBLK = (BLK / 8) * CH;  // 8x8 blocks of V
-      const uint4* kg = (const uint4*)((const uint16_t*)a.k + ((size_t)page * sq.h_kv + g) * BLK * D);
-      const uint4* vg = (const uint4*)((const uint16_t*)a.v + ((size_t)page * sq.h_kv + g) * BLK * D);
-      uint4 kr[KPT];
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int c = i * C::THREADS + tid;
-        kr[i] = (c / CH) < nvalid ? kg[c] : make_uint4(0, 0, 0, 0);
-      }
-      uint32_t vr[8][4];
-      const int vdch = tid % CH, vkg = tid / CH;
-      if (tid < VBLK) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int key = vkg * 8 + i;
-          uint4 x = key < nvalid ? vg[key * CH + vdch] : make_uint4(0, 0, 0, 0);
-          vr[i][0] = x.x;
-          vr[i][1] = x.y;
-          vr[i][2] = x.z;
-          vr[i][3] = x.w;
-        }
-      }
-      __syncthreads();  // every wave is done with the previous tiles
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int c = i * C::THREADS + tid;
-        *(uint4*)(k_lds + (c / CH) * C::K_PITCH + (c % CH) * 16) = kr[i];
-      }
-      if (tid < VBLK) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          // row d = vdch*8 + j of V^T: keys vkg*8 .. vkg*8+7
-          uint32_t o4[4];
-#pragma unroll
-          for (int p = 0; p < 4; ++p) o4[p] = pack_halves(vr[2 * p][j / 2], vr[2 * p + 1][j / 2], j & 1);
-          unsigned char* dst = v_lds + (vdch * 8 + j) * C::V_PITCH + vkg * 16;
-          *(uint2*)dst = make_uint2(o4[0], o4[1]);
-          *(uint2*)(dst + 8) = make_uint2(o4[2], o4[3]);
-        }
-      }
-      __syncthreads();
-    } else {
-      constexpr int CH = D / 4;  // 16-byte chunks per key row
-      constexpr int KPT = BLK * CH / C::THREADS;
-      const float4* kg = (const float4*)((const float*)a.k + ((size_t)page * sq.h_kv + g) * BLK * D);
-      const float4* vg = (const float4*)((const float*)a.v + ((size_t)page * sq.h_kv + g) * BLK * D);
-      float4 kr[KPT], vr[KPT];
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int c = i * C::THREADS + tid;
-        const bool ok = (c / CH) < nvalid;
-        kr[i] = ok ? kg[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-        vr[i] = ok ? vg[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int c = i * C::THREADS + tid;
-        float* kd = (float*)(k_lds + (c / CH) * C::K_PITCH) + (c % CH) * 4;
-        float* vd = (float*)(v_lds + (c / CH) * C::V_PITCH) + (c % CH) * 4;
-        kd[0] = kr[i].x; kd[1] = kr[i].y; kd[2] = kr[i].z; kd[3] = kr[i].w;
-        vd[0] = vr[i].x; vd[1] = vr[i].y; vd[2] = vr[i].z; vd[3] = vr[i].w;
-      }
-      __syncthreads();
-    }
+  for (int t = 0; t < n_list; ++t) {
+    int nkey0 = 0;
+    size_t nelem = 0;
+    const bool more = t + 1 < n_list;
+    if (more) locate(t + 1, nkey0, nelem);
+
+    __syncthreads();  // A: PV(t-1) done everywhere; K(t) visible
+    stg.store_v(v_lds, tid);
+    if (more) stg.load_k(kbase + nelem * ES, min(BLK, Lk - nkey0), tid);
 
     // ---- S^T = K Q^T for this wave's 32 rows ------------------------------
+    // k-step outer, key tile inner: KT independent accumulators per k-step.
     f32x16 s[C::KT];
 #pragma unroll
-    for (int kt = 0; kt < C::KT; ++kt) {
+    for (int kt = 0; kt < C::KT; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[kt][v] = 0.f;
-      if constexpr (BF16) {
-        const unsigned char* kp = k_lds + (kt * 32 + l32) * C::K_PITCH + hl * 16;
+    if constexpr (BF16) {
+      const unsigned char* kp = k_lds + l32 * C::K_PITCH + hl * 16;
 #pragma unroll
-        for (int ks = 0; ks < C::QREGS; ++ks) {
-          bf16x8 kf = *(const bf16x8*)(kp + ks * 32);
+      for (int ks = 0; ks < C::QREGS; ++ks) {
+#pragma unroll
+        for (int kt = 0; kt < C::KT; ++kt) {
+          const bf16x8 kf = *(const bf16x8*)(kp + kt * 32 * C::K_PITCH + ks * 32);
           s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf16[ks], s[kt], 0, 0, 0);
         }
-      } else {
-        const float* kp = (const float*)(k_lds + (kt * 32 + l32) * C::K_PITCH) + hl;
-#pragma unroll
-        for (int ks = 0; ks < C::QREGS; ++ks)
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x2f32(kp[2 * ks], qf32[ks], s[kt], 0, 0, 0);
       }
+    } else {
+      const float* kp = (const float*)(k_lds + l32 * C::K_PITCH) + hl;
+#pragma unroll
+      for (int ks = 0; ks < C::QREGS; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < C::KT; ++kt)
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x2f32(kp[kt * 32 * (C::K_PITCH / 4) + 2 * ks], qf32[ks],
+                                                       s[kt], 0, 0, 0);
     }
     // causal mask: element (kt, v) is key kt*32 + 8*(v/4) + 4*hl + v%4
     if (key0 + BLK - 1 > off + qb * BLK) {
@@ -285,26 +335,31 @@ __global__ __launch_bounds__(2 * BLK) void osk_kernel(OskArgs a) {  // 2*BLK == 
       for (int v = 0; v < 16; ++v) m_loc = fmaxf(m_loc, s[kt][v]);
     m_loc = fmaxf(m_loc, __shfl_xor(m_loc, 32));
 
-    // ---- in-kernel skip test over all rows of the query block --------------
-    bool skip = false;
+    // ---- per-tile skip margin: max over the wave's valid rows --------------
     if constexpr (!DENSE) {
       if (a.skip_on) {
         float diff = (row_valid && m_loc != kNegInf) ? m_loc - m_run : kNegInf;
         diff = wave_max32(diff);
         if (lane == 0) red[w] = diff;
-        __syncthreads();
+      }
+    }
+    __syncthreads();  // C: K(t) reads done everywhere; V(t) and margins visible
+    if (more) {
+      stg.store_k(k_lds, tid);
+      stg.load_v(vbase + nelem * ES, min(BLK, Lk - nkey0), tid);
+    }
+    key0 = nkey0;  // for the next iteration's mask (set before a possible skip)
+    bool skip = false;
+    if constexpr (!DENSE) {
+      if (a.skip_on) {
         float worst = red[0];
 #pragma unroll
         for (int i = 1; i < C::NW; ++i) worst = fmaxf(worst, red[i]);
         skip = worst < a.skip_thr_raw;
       }
-      if (tid == 0 && a.skip_bits) a.skip_bits[out_row * a.kmax + t] = skip ? 1 : 0;
     }
-    if (skip) {
-      ++n_skip;
-      continue;
-    }
-
+    n_skip += skip ? 1 : 0;
+    if (!skip) {
     // ---- online-softmax update ---------------------------------------------
     const float m_new = fmaxf(m_run, m_loc);
     const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
@@ -320,10 +375,12 @@ __global__ __launch_bounds__(2 * BLK) void osk_kernel(OskArgs a) {  // 2*BLK == 
       }
     l_run = l_run * alpha + rs;
     m_run = m_new;
+    if (__any(alpha != 1.f)) {  // rescale only when some row's max moved
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
+      for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[dt][v] *= alpha;
+        for (int v = 0; v < 16; ++v) acc[dt][v] *= alpha;
+    }
 
     // ---- O^T += V^T P^T ----------------------------------------------------
     if constexpr (BF16) {
@@ -334,19 +391,20 @@ __global__ __launch_bounds__(2 * BLK) void osk_kernel(OskArgs a) {  // 2*BLK == 
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
           for (int i = 0; i < 8; ++i) pb[kt][s2][i] = (__bf16)s[kt][8 * s2 + i];
+      // k-step outer (16 keys), head-dim tile inner: DT independent accumulators
+      const unsigned char* vp = v_lds + l32 * C::V_PITCH + hl * 8;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        const unsigned char* vp = v_lds + (dt * 32 + l32) * C::V_PITCH + hl * 8;
+      for (int kt = 0; kt < C::KT; ++kt)
 #pragma unroll
-        for (int kt = 0; kt < C::KT; ++kt)
+        for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const uint2 lo = *(const uint2*)(vp + (kt * 32 + 16 * s2) * 2);
-            const uint2 hi = *(const uint2*)(vp + (kt * 32 + 16 * s2 + 8) * 2);
+          for (int dt = 0; dt < C::DT; ++dt) {
+            const unsigned char* vr = vp + dt * 32 * C::V_PITCH + (kt * 32 + 16 * s2) * 2;
+            const uint2 lo = *(const uint2*)vr;
+            const uint2 hi = *(const uint2*)(vr + 16);
             const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
             acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kt][s2], acc[dt], 0, 0, 0);
           }
-      }
     } else {
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
@@ -358,6 +416,10 @@ __global__ __launch_bounds__(2 * BLK) void osk_kernel(OskArgs a) {  // 2*BLK == 
             const float vf = *((const float*)(v_lds + key * C::V_PITCH) + dt * 32 + l32);
             acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf, s[kt][v], acc[dt], 0, 0, 0);
           }
+    }
+    }  // !skip
+    if constexpr (!DENSE) {
+      if (tid == 0 && a.skip_bits) a.skip_bits[out_row * a.kmax + t] = skip ? 1 : 0;
     }
   }
 
@@ -417,17 +479,13 @@ hipError_t launch_one(const OskArgs& a, bool dense, hipStream_t stream) {
 
 hipError_t launch_osk(const OskArgs& a, int dtype, int head_dim, int block, bool dense,
                       hipStream_t stream) {
-  const bool bf = dtype == 1;
-#define COSA_OSK_CASE(BF, DD, BB) \
-  if (bf == BF && head_dim == DD && block == BB) return launch_one<BF, DD, BB>(a, dense, stream);
-  COSA_OSK_CASE(true, 128, 128)
-  COSA_OSK_CASE(true, 128, 64)
-  COSA_OSK_CASE(true, 64, 128)
-  COSA_OSK_CASE(true, 64, 64)
-  COSA_OSK_CASE(false, 128, 128)
-  COSA_OSK_CASE(false, 128, 64)
-  COSA_OSK_CASE(false, 64, 128)
-  COSA_OSK_CASE(false, 64, 64)
+  if (dtype == 1) return launch_osk_bf16(a, head_dim, block, dense, stream);
+#define COSA_OSK_CASE(DD, BB) \
+  if (head_dim == DD && block == BB) return launch_one<false, DD, BB>(a, dense, stream);
+  COSA_OSK_CASE(128, 128)
+  COSA_OSK_CASE(128, 64)
+  COSA_OSK_CASE(64, 128)
+  COSA_OSK_CASE(64, 64)
 #undef COSA_OSK_CASE
   return hipErrorInvalidValue;
 }

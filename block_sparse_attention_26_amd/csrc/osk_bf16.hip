@@ -1,0 +1,382 @@
+// Ordered-Skipping Kernel (OSK) and dense baseline, bf16 path for gfx950.
+//
+// Method: CoSA technical summary (gist.science, "CoSA: Accelerating
+// Long-Context Inference via Proxy-Kernel Co-Designed Sparse Attention"),
+// §2.3 (walk only the listed pages, in order; skip a retained block in-kernel
+// from the local vs running row maxima; otherwise compute it), §2.1 (the
+// online-softmax result does not depend on the visit order) and §1 (the skip
+// veto is per tile: every row of the query block must agree).
+//
+// One workgroup per (sequence, query head, query block): B/32 waves of 32
+// query rows. Scores are formed transposed, S^T = K Q^T, with
+// v_mfma_f32_32x32x16_bf16, so each lane owns one query row; the output is
+// accumulated transposed too, O^T += V^T P^T, with the bf16 P registers as the
+// B operand.
+//
+// gfx950 data movement:
+//  * K and V pages are copied global -> LDS by global_load_lds_dwordx4 (no
+//    staging registers). Lane l of a load lands at LDS base + 16*l, so the
+//    tiles are XOR-swizzled by choosing each lane's source chunk: K rows are
+//    swizzled by (row mod 16) so the 32 rows read by one MFMA operand fetch
+//    spread over all banks; V rows by 4*(row mod 4) for the transposed reads.
+//  * V^T operands come from ds_read_b64_tr_b16: in each 16-lane group, lanes
+//    4k..4k+3 address 4 consecutive head-dim columns of key row K_k and every
+//    lane receives 4 keys of one column.
+//  * Per listed block: barrier A (K(t) landed, V buffer free) -> copy V(t)
+//    -> S(t) = K(t) Q^T, mask, row maxima, per-wave skip margin -> barrier C
+//    (V(t) landed, K buffer free, margins visible) -> copy K(t+1) -> unless
+//    skipped, softmax and O^T += V(t)^T P(t)^T. Tiles are single-buffered
+//    (64 KB of LDS) so two workgroups share a CU: one's MFMA work overlaps the
+//    other's softmax and copy waits.
+// Tail keys (past the sequence end) are loaded from a valid key row of the
+// same page and masked, so NaN-filled slots never reach the MFMAs.
+#include <math.h>
+
+#include "cosa_internal.h"
+
+namespace cosa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float wave_max32(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 8));
+  x = fmaxf(x, __shfl_xor(x, 4));
+  x = fmaxf(x, __shfl_xor(x, 2));
+  x = fmaxf(x, __shfl_xor(x, 1));
+  return x;
+}
+
+template <int D, int BLK>
+struct Geo {
+  static constexpr int NW = BLK / 32;
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int KT = BLK / 32;         // 32-key tiles per block
+  static constexpr int DT = D / 32;           // 32-column tiles of O
+  static constexpr int QREGS = D / 16;        // k-steps of S
+  static constexpr int CH = D / 8;            // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;          // bytes per row
+  static constexpr int TILE = BLK * ROWB;     // bytes per K or V tile
+  static constexpr int NL = TILE / 1024 / NW; // 1 KB DMA copies per wave per tile
+  static constexpr int RPC = 1024 / ROWB;     // rows per 1 KB copy
+  __device__ static constexpr int swz_k(int r) { return r % CH; }
+  __device__ static constexpr int swz_v(int r) { return D == 128 ? 4 * (r % 4) : 4 * (r % 2); }
+};
+
+template <int D, int BLK, bool DENSE>
+__global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
+  using Gm = Geo<D, BLK>;
+  constexpr int NW = Gm::NW, KT = Gm::KT, DT = Gm::DT, QREGS = Gm::QREGS;
+  constexpr int CH = Gm::CH, ROWB = Gm::ROWB, TILE = Gm::TILE, NL = Gm::NL, RPC = Gm::RPC;
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[TILE];
+  __shared__ float red[NW];
+
+  const SeqArgs& sq = a.seq;
+  const int G = sq.group;
+  // ---- unit decode: XCD-grouped, longest query block first --------------
+  const int64_t bid = blockIdx.x;
+  const int64_t xcd = bid % kNumXcd, slot = bid / kNumXcd;
+  const int64_t lam = ((slot / G) * kNumXcd + xcd) * G + slot % G;
+  if (lam >= a.n_units) return;
+  const int hig = (int)(lam % G);
+  int64_t rest = lam / G;
+  const int g = (int)(rest % sq.h_kv);
+  rest /= sq.h_kv;
+  const int b = (int)(rest % sq.batch);
+  const int qb = sq.max_nq - 1 - (int)(rest / sq.batch);
+  const int h = g * G + hig;
+  const int q0 = sq.cu_seqlens_q[b];
+  const int Lq = sq.cu_seqlens_q[b + 1] - q0;
+  const int Lk = sq.seqlens_k[b];
+  const int tid = threadIdx.x;
+  const int64_t out_row = ((int64_t)b * sq.h_q + h) * sq.max_nq + qb;
+  if (qb * BLK >= Lq) {  // past this sequence's end: an empty row
+    if constexpr (!DENSE) {
+      if (tid == 0) {
+        a.visited[out_row] = 0;
+        a.skipped[out_row] = 0;
+      }
+      if (a.skip_bits)
+        for (int t = tid; t < a.kmax; t += Gm::THREADS) a.skip_bits[out_row * a.kmax + t] = 255;
+    }
+    return;
+  }
+  const int off = Lk - Lq;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+  const int row = w * 32 + l32;
+  const bool row_valid = qb * BLK + row < Lq;
+  const int my_pos = off + qb * BLK + row;
+  const int n_causal = (off + min(qb * BLK + BLK - 1, Lq - 1)) / BLK + 1;
+  const int diag_key0 = off + qb * BLK - (BLK - 1);  // blocks starting after this need the mask
+
+  // ---- query fragments (B operand of S^T = K Q^T) -------------------------
+  bf16x8 qf[QREGS];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(q0 + qb * BLK + row) * sq.h_q + h) * D + hl * 8;
+#pragma unroll
+    for (int ks = 0; ks < QREGS; ++ks) {
+      const uint4 x = row_valid ? *(const uint4*)(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+      qf[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  int n_list;
+  const int32_t* lst = nullptr;
+  if constexpr (DENSE) {
+    n_list = n_causal;
+  } else {
+    const int64_t list_row = ((int64_t)b * sq.h_kv + g) * sq.max_nq + qb;
+    n_list = min(a.count[list_row], a.kmax);  // a corrupt count cannot overrun the row
+    lst = a.order + list_row * a.kmax;
+  }
+  int bad = 0;
+  const int32_t* table = sq.block_table + (int64_t)b * sq.max_blocks_k;
+  const unsigned char* kglob = (const unsigned char*)a.k + (size_t)g * TILE;
+  const unsigned char* vglob = (const unsigned char*)a.v + (size_t)g * TILE;
+  const size_t page_bytes = (size_t)sq.h_kv * TILE;
+
+  // ---- per-lane DMA source offsets (bytes within a page slab) ------------
+  // Copy n of wave w fills LDS bytes [(w*NL + n) * 1024, +1024): row
+  // r = (w*NL + n)*RPC + lane/CH, physical chunk lane%CH, which must hold the
+  // logical chunk (lane%CH) ^ swz(r). With NL a multiple of 4 (d = 128) the
+  // K swizzle depends on n mod 4 only; with RPC a multiple of CH (d = 64) on
+  // the lane only; the V swizzle depends on the lane only in both cases.
+  static_assert(D == 64 || NL % 4 == 0, "K swizzle period");
+  static_assert(D == 128 || RPC % CH == 0, "K swizzle period");
+  const uint32_t dma_lane = (uint32_t)((lane / CH) * ROWB);
+  uint32_t dma_kx[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = u * RPC + lane / CH;  // a row with the same K swizzle as copy n = u (mod 4)
+    dma_kx[u] = dma_lane + (uint32_t)(((lane % CH) ^ Gm::swz_k(r)) * 16);
+  }
+  const uint32_t dma_vx = dma_lane + (uint32_t)(((lane % CH) ^ Gm::swz_v(lane / CH)) * 16);
+  // Copy the K (or V) tile of list entry t into LDS. Rows past the sequence
+  // end re-read the last valid row (their scores are masked). Returns kb.
+  auto dma_tile = [&](int t, bool is_k) -> int {
+    int kb = DENSE ? t : lst[t];
+    if (kb < 0 || kb >= n_causal) {
+      bad = 1;
+      kb = 0;
+    }
+    int page = table[kb];
+    if ((unsigned)page >= (unsigned)sq.num_pages) {
+      bad = 1;
+      page = 0;
+    }
+    const int nvalid = min(BLK, Lk - kb * BLK);
+    const unsigned char* src = (is_k ? kglob : vglob) + (size_t)page * page_bytes;
+    unsigned char* dst = (is_k ? kbuf : vbuf) + w * NL * 1024;
+    if (nvalid >= BLK) {
+      const unsigned char* wsrc = src + (size_t)w * NL * 1024;
+#pragma unroll
+      for (int n = 0; n < NL; ++n) {
+        const uint32_t o = (is_k ? dma_kx[n % 4] : dma_vx) + (uint32_t)(n * 1024);
+        __builtin_amdgcn_global_load_lds((const void*)(wsrc + o), (lds_void*)(dst + n * 1024), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NL; ++n) {
+        const int r = (w * NL + n) * RPC + lane / CH;
+        const int sw = is_k ? Gm::swz_k(r) : Gm::swz_v(r);
+        const uint32_t o = (uint32_t)(min(r, nvalid - 1) * ROWB + (((lane % CH) ^ sw) * 16));
+        __builtin_amdgcn_global_load_lds((const void*)(src + o), (lds_void*)(dst + n * 1024), 16, 0, 0);
+      }
+    }
+    return kb;
+  };
+
+  // ---- operand addressing ---------------------------------------------------
+  // K (A operand of S^T): row kt*32 + l32, logical chunk 2*ks + hl.
+  const unsigned char* k_lane = kbuf + l32 * ROWB;
+  const int k_swz = Gm::swz_k(l32);
+  // V^T (A operand of O^T) via ds_read_b64_tr_b16: lane group gi = lane/16,
+  // i = lane%16 reads key row 4*hh + i/4 (+ 16*step + 8*half), columns
+  // dt*32 + 16*dg + 4*(i%4) .. +3.
+  int v_addr[DT];
+  {
+    const int i = lane & 15, gi = lane >> 4, hh = gi >> 1, dg = gi & 1;
+    const int q = i >> 2;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = dt * 32 + 16 * dg + 4 * (i & 3);
+      v_addr[dt] = (4 * hh + q) * ROWB + (((d >> 3) ^ Gm::swz_v(q)) << 4) + (d & 7) * 2;
+    }
+  }
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[dt][v] = 0.f;
+  float m_run = kNegInf;  // running max of raw q.k (unscaled)
+  float l_run = 0.f;      // this lane's share of the running sum
+  int n_skip = 0;
+  const float c2 = a.scale_log2;
+
+  int kb = dma_tile(0, true);  // K(0)
+  for (int t = 0; t < n_list; ++t) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // A: K(t) landed; every wave is done with V(t-1)
+    dma_tile(t, false);  // V(t)
+
+    // ---- S^T = K Q^T for this wave's 32 rows -------------------------------
+    f32x16 s[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[kt][v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < QREGS; ++ks) {
+      const unsigned char* kp = k_lane + (((2 * ks + hl) ^ k_swz) << 4);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const bf16x8 kf = *(const bf16x8*)(kp + kt * 32 * ROWB);
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kt], 0, 0, 0);
+      }
+    }
+    // causal mask (only blocks that reach past the first row's position)
+    if (kb * BLK > diag_key0) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kb * BLK + kt * 32 + 8 * (v >> 2) + 4 * hl + (v & 3);
+          if (key > my_pos) s[kt][v] = kNegInf;
+        }
+    }
+    float m_loc = kNegInf;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) m_loc = fmaxf(m_loc, s[kt][v]);
+    m_loc = fmaxf(m_loc, __shfl_xor(m_loc, 32));
+    if constexpr (!DENSE) {
+      if (a.skip_on) {
+        float diff = (row_valid && m_loc != kNegInf) ? m_loc - m_run : kNegInf;
+        diff = wave_max32(diff);
+        if (lane == 0) red[w] = diff;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // C: V(t) landed; every wave is done with K(t); margins visible
+    bool skip = false;
+    if constexpr (!DENSE) {
+      if (a.skip_on) {
+        float worst = red[0];
+#pragma unroll
+        for (int i = 1; i < NW; ++i) worst = fmaxf(worst, red[i]);
+        skip = __builtin_amdgcn_readfirstlane(worst < a.skip_thr_raw ? 1 : 0) != 0;
+      }
+    }
+    const int kb_next = (t + 1 < n_list) ? dma_tile(t + 1, true) : 0;  // K(t+1)
+
+    // ---- online-softmax update (its results are dropped when skipped) -----
+    const float m_new = skip ? m_run : fmaxf(m_run, m_loc);
+    const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+    const float mc = (m_new == kNegInf) ? 0.f : m_new * c2;
+    bf16x8 pb[KT][2];
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][v], c2, -mc));
+        rs += p;
+        pb[kt][v >> 3][v & 7] = (__bf16)p;
+      }
+    l_run = skip ? l_run : l_run * alpha + rs;
+    m_run = m_new;
+    n_skip += skip ? 1 : 0;
+    if (__any(alpha != 1.f)) {  // rescale only when some row's max moved
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[dt][v] *= alpha;
+    }
+    if (!skip) {
+      // ---- O^T += V^T P^T (k-steps of 16 keys) -------------------------------
+#pragma unroll
+      for (int st = 0; st < 2 * KT; ++st)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const unsigned char* vp = vbuf + v_addr[dt] + st * 16 * ROWB;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * ROWB));
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[st >> 1][st & 1], acc[dt], 0, 0, 0);
+        }
+    }
+    if constexpr (!DENSE) {
+      if (tid == 0 && a.skip_bits) a.skip_bits[out_row * a.kmax + t] = skip ? 1 : 0;
+    }
+    kb = kb_next;
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (bad) inv = __builtin_nanf("");
+  if (row_valid) {
+    const size_t ooff = ((size_t)(q0 + qb * BLK + row) * sq.h_q + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = dt * 32 + 8 * g4 + 4 * hl;
+        const float o0 = acc[dt][4 * g4 + 0] * inv, o1 = acc[dt][4 * g4 + 1] * inv;
+        const float o2 = acc[dt][4 * g4 + 2] * inv, o3 = acc[dt][4 * g4 + 3] * inv;
+        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o0) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o1) << 16);
+        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o2) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o3) << 16);
+        *(uint2*)((uint16_t*)a.o + ooff + d0) = make_uint2(lo, hi);
+      }
+    if (a.lse && hl == 0) {
+      a.lse[(size_t)h * a.total_q + q0 + qb * BLK + row] =
+          bad ? __builtin_nanf("") : (l_tot > 0.f ? m_run * a.scale + logf(l_tot) : kNegInf);
+    }
+  }
+  if constexpr (!DENSE) {
+    if (tid == 0) {
+      a.visited[out_row] = n_list;
+      a.skipped[out_row] = n_skip;
+    }
+    if (a.skip_bits)
+      for (int t = n_list + tid; t < a.kmax; t += Gm::THREADS) a.skip_bits[out_row * a.kmax + t] = 255;
+  }
+}
+
+template <int D, int BLK>
+hipError_t launch_one(const OskArgs& a, bool dense, hipStream_t stream) {
+  const int64_t per = (int64_t)kNumXcd * a.seq.group;
+  const int64_t grid = (a.n_units + per - 1) / per * per;
+  if (dense)
+    hipLaunchKernelGGL((osk_bf16_kernel<D, BLK, true>), dim3((unsigned)grid), dim3(2 * BLK), 0, stream, a);
+  else
+    hipLaunchKernelGGL((osk_bf16_kernel<D, BLK, false>), dim3((unsigned)grid), dim3(2 * BLK), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_osk_bf16(const OskArgs& a, int head_dim, int block, bool dense, hipStream_t stream) {
+  if (head_dim == 128 && block == 128) return launch_one<128, 128>(a, dense, stream);
+  if (head_dim == 128 && block == 64) return launch_one<128, 64>(a, dense, stream);
+  if (head_dim == 64 && block == 128) return launch_one<64, 128>(a, dense, stream);
+  if (head_dim == 64 && block == 64) return launch_one<64, 64>(a, dense, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace cosa
