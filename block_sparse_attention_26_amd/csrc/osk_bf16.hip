@@ -93,9 +93,10 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
   const int b = (int)(rest % sq.batch);
   const int qb = sq.max_nq - 1 - (int)(rest / sq.batch);
   const int h = g * G + hig;
-  const int q0 = sq.cu_seqlens_q[b];
-  const int Lq = sq.cu_seqlens_q[b + 1] - q0;
-  const int Lk = sq.seqlens_k[b];
+  // sequence metadata is uniform: keep it in scalar registers
+  const int q0 = __builtin_amdgcn_readfirstlane(sq.cu_seqlens_q[b]);
+  const int Lq = __builtin_amdgcn_readfirstlane(sq.cu_seqlens_q[b + 1]) - q0;
+  const int Lk = __builtin_amdgcn_readfirstlane(sq.seqlens_k[b]);
   const int tid = threadIdx.x;
   const int64_t out_row = ((int64_t)b * sq.h_q + h) * sq.max_nq + qb;
   if (qb * BLK >= Lq) {  // past this sequence's end: an empty row
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
     n_list = n_causal;
   } else {
     const int64_t list_row = ((int64_t)b * sq.h_kv + g) * sq.max_nq + qb;
-    n_list = min(a.count[list_row], a.kmax);  // a corrupt count cannot overrun the row
+    n_list = min(__builtin_amdgcn_readfirstlane(a.count[list_row]), a.kmax);  // a corrupt count cannot overrun the row
     lst = a.order + list_row * a.kmax;
   }
   int bad = 0;
@@ -165,12 +166,12 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
   // Copy the K (or V) tile of list entry t into LDS. Rows past the sequence
   // end re-read the last valid row (their scores are masked). Returns kb.
   auto dma_tile = [&](int t, bool is_k) -> int {
-    int kb = DENSE ? t : lst[t];
+    int kb = DENSE ? t : __builtin_amdgcn_readfirstlane(lst[t]);  // uniform: keeps the mask branch scalar
     if (kb < 0 || kb >= n_causal) {
       bad = 1;
       kb = 0;
     }
-    int page = table[kb];
+    int page = __builtin_amdgcn_readfirstlane(table[kb]);
     if ((unsigned)page >= (unsigned)sq.num_pages) {
       bad = 1;
       page = 0;
@@ -232,29 +233,45 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
     dma_tile(t, false);  // V(t)
 
     // ---- S^T = K Q^T for this wave's 32 rows -------------------------------
+    // fragments of k-step ks+1 are read while the MFMAs of k-step ks run
     f32x16 s[KT];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[kt][v] = 0.f;
+    {
+      bf16x8 kf[2][KT];
 #pragma unroll
-    for (int ks = 0; ks < QREGS; ++ks) {
-      const unsigned char* kp = k_lane + (((2 * ks + hl) ^ k_swz) << 4);
+      for (int kt = 0; kt < KT; ++kt) kf[0][kt] = *(const bf16x8*)(k_lane + ((hl ^ k_swz) << 4) + kt * 32 * ROWB);
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const bf16x8 kf = *(const bf16x8*)(kp + kt * 32 * ROWB);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kt], 0, 0, 0);
+      for (int ks = 0; ks < QREGS; ++ks) {
+        if (ks + 1 < QREGS) {
+          const unsigned char* kp = k_lane + (((2 * (ks + 1) + hl) ^ k_swz) << 4);
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) kf[(ks + 1) & 1][kt] = *(const bf16x8*)(kp + kt * 32 * ROWB);
+        }
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks & 1][kt], qf[ks], s[kt], 0, 0, 0);
+      }
+      // pin the order: the reads of step ks+1 are issued ahead of the MFMAs of step ks
+      __builtin_amdgcn_sched_group_barrier(0x100, KT, 0);  // DS reads (step 0)
+#pragma unroll
+      for (int ks = 0; ks < QREGS; ++ks) {
+        if (ks + 1 < QREGS) __builtin_amdgcn_sched_group_barrier(0x100, KT, 0);  // DS reads (step ks+1)
+        __builtin_amdgcn_sched_group_barrier(0x008, KT, 0);                       // MFMA (step ks)
       }
     }
-    // causal mask (only blocks that reach past the first row's position)
+    // causal mask (only blocks that reach past the first row's position):
+    // element (kt, v) is key kb*B + kt*32 + 8*(v/4) + 4*hl + v%4
     if (kb * BLK > diag_key0) {
+      asm volatile("" ::: "memory");  // keep this a real branch (no if-conversion)
+      const int thr = my_pos - kb * BLK - 4 * hl;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kb * BLK + kt * 32 + 8 * (v >> 2) + 4 * hl + (v & 3);
-          if (key > my_pos) s[kt][v] = kNegInf;
-        }
+        for (int v = 0; v < 16; ++v)
+          if (kt * 32 + 8 * (v >> 2) + (v & 3) > thr) s[kt][v] = kNegInf;
     }
     float m_loc = kNegInf;
 #pragma unroll
@@ -306,17 +323,38 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
         for (int v = 0; v < 16; ++v) acc[dt][v] *= alpha;
     }
     if (!skip) {
-      // ---- O^T += V^T P^T (k-steps of 16 keys) -------------------------------
+      // ---- O^T += V^T P^T (k-steps of 16 keys), fragments one step ahead -----
+      auto vread = [&](int st, int dt, int e) -> s16x4 {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(vbuf + v_addr[dt] + (st * 16 + 8 * e) * ROWB));
+      };
+      s16x4 vf[2][DT][2];
 #pragma unroll
-      for (int st = 0; st < 2 * KT; ++st)
+      for (int dt = 0; dt < DT; ++dt) {
+        vf[0][dt][0] = vread(0, dt, 0);
+        vf[0][dt][1] = vread(0, dt, 1);
+      }
+#pragma unroll
+      for (int st = 0; st < 2 * KT; ++st) {
+        if (st + 1 < 2 * KT)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            vf[(st + 1) & 1][dt][0] = vread(st + 1, dt, 0);
+            vf[(st + 1) & 1][dt][1] = vread(st + 1, dt, 1);
+          }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const unsigned char* vp = vbuf + v_addr[dt] + st * 16 * ROWB;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * ROWB));
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[st >> 1][st & 1], acc[dt], 0, 0, 0);
+          const bf16x8 vv = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(vf[st & 1][dt][0], vf[st & 1][dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[st >> 1][st & 1], acc[dt], 0, 0, 0);
         }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT, 1);  // DS reads (step 0)
+#pragma unroll
+      for (int st = 0; st < 2 * KT; ++st) {
+        if (st + 1 < 2 * KT) __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT, 1);  // reads (st+1)
+        __builtin_amdgcn_sched_group_barrier(0x008, DT, 1);                            // MFMA (st)
+      }
     }
     if constexpr (!DENSE) {
       if (tid == 0 && a.skip_bits) a.skip_bits[out_row * a.kmax + t] = skip ? 1 : 0;
