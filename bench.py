@@ -60,6 +60,28 @@ def parse():
     return ap.parse_args()
 
 
+OSK_SOURCE = os.path.join(ROOT, "block_sparse_attention_26_amd", "csrc", "osk_bf16.hip")
+HBM_PROFILE = os.path.join(ROOT, "profiles", "hbm_counters_128k_b10.md")
+
+
+def profiled_traffic():
+    """HBM bytes per OSK launch from the committed counter summary, or None
+    when the summary was taken on a different kernel source."""
+    import hashlib
+    import re
+
+    try:
+        src = hashlib.sha256(open(OSK_SOURCE, "rb").read()).hexdigest()
+        text = open(HBM_PROFILE).read()
+    except OSError:
+        return None
+    m_src = re.search(r"osk_bf16\.hip sha256: ([0-9a-f]{64})", text)
+    m_val = re.search(r"osk HBM bytes per launch: ([0-9.eE+]+)", text)
+    if not (m_src and m_val) or m_src.group(1) != src:
+        return None
+    return float(m_val.group(1))
+
+
 def cpu_baseline(case, kap_count, seconds_target=20.0):
     """Time the oracle on KV group 0: its whole proxy, then its ordered walk
     over evenly spaced query blocks until about `seconds_target` seconds of
@@ -280,7 +302,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": osk_tflops / peak,
-            "traffic": None,
+            "traffic": profiled_traffic() if args.workload == "cfg3" and abs(case.budget - 0.1) < 1e-12 else None,
             "algorithmic_flops_per_launch": osk_flops,
         },
         "cpu_baseline": cpu,
