@@ -299,31 +299,29 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
     }
     const int kb_next = (t + 1 < n_list) ? dma_tile(t + 1, true) : 0;  // K(t+1)
 
-    // ---- online-softmax update (its results are dropped when skipped) -----
-    const float m_new = skip ? m_run : fmaxf(m_run, m_loc);
-    const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-    const float mc = (m_new == kNegInf) ? 0.f : m_new * c2;
-    bf16x8 pb[KT][2];
-    float rs = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][v], c2, -mc));
-        rs += p;
-        pb[kt][v >> 3][v & 7] = (__bf16)p;
-      }
-    l_run = skip ? l_run : l_run * alpha + rs;
-    m_run = m_new;
+    // ---- online-softmax update and O^T += V^T P^T, one 32-key tile at a time:
+    // the exps of tile kt+1 (VALU) run while the P.V MFMAs of tile kt execute
     n_skip += skip ? 1 : 0;
-    if (__any(alpha != 1.f)) {  // rescale only when some row's max moved
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[dt][v] *= alpha;
-    }
     if (!skip) {
-      // ---- O^T += V^T P^T (k-steps of 16 keys), fragments one step ahead -----
+      const float m_new = fmaxf(m_run, m_loc);
+      const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      const float mc = (m_new == kNegInf) ? 0.f : m_new * c2;
+      if (__any(alpha != 1.f)) {  // rescale only when some row's max moved
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[dt][v] *= alpha;
+      }
+      m_run = m_new;
+      float rs = 0.f;
+      auto ptile = [&](int kt, bf16x8 (&pd)[2]) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][v], c2, -mc));
+          rs += p;
+          pd[v >> 3][v & 7] = (__bf16)p;
+        }
+      };
       auto vread = [&](int st, int dt, int e) -> s16x4 {
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4*)(vbuf + v_addr[dt] + (st * 16 + 8 * e) * ROWB));
@@ -334,27 +332,29 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
         vf[0][dt][0] = vread(0, dt, 0);
         vf[0][dt][1] = vread(0, dt, 1);
       }
+      bf16x8 pt[2][2];
+      ptile(0, pt[0]);
 #pragma unroll
-      for (int st = 0; st < 2 * KT; ++st) {
-        if (st + 1 < 2 * KT)
+      for (int kt = 0; kt < KT; ++kt) {
+        if (kt + 1 < KT) ptile(kt + 1, pt[(kt + 1) & 1]);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int st = 2 * kt + s2;
+          if (st + 1 < 2 * KT)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+              vf[(st + 1) & 1][dt][0] = vread(st + 1, dt, 0);
+              vf[(st + 1) & 1][dt][1] = vread(st + 1, dt, 1);
+            }
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            vf[(st + 1) & 1][dt][0] = vread(st + 1, dt, 0);
-            vf[(st + 1) & 1][dt][1] = vread(st + 1, dt, 1);
+            const bf16x8 vv = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(vf[st & 1][dt][0], vf[st & 1][dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pt[kt & 1][s2], acc[dt], 0, 0, 0);
           }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8 vv = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(vf[st & 1][dt][0], vf[st & 1][dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[st >> 1][st & 1], acc[dt], 0, 0, 0);
         }
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT, 1);  // DS reads (step 0)
-#pragma unroll
-      for (int st = 0; st < 2 * KT; ++st) {
-        if (st + 1 < 2 * KT) __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT, 1);  // reads (st+1)
-        __builtin_amdgcn_sched_group_barrier(0x008, DT, 1);                            // MFMA (st)
-      }
+      l_run = l_run * alpha + rs;
     }
     if constexpr (!DENSE) {
       if (tid == 0 && a.skip_bits) a.skip_bits[out_row * a.kmax + t] = skip ? 1 : 0;
