@@ -275,12 +275,14 @@ __global__ __launch_bounds__(2 * BLK, 1) void osk_kernel(OskArgs a) {  // 2*BLK 
 
   // ---- prologue: K(0) into LDS, V(0) into the staging registers -----------
   S stg;
-  int key0;
-  size_t elem;
-  locate(0, key0, elem);
-  stg.load_k(kbase + elem * ES, min(BLK, Lk - key0), tid);
-  stg.store_k(k_lds, tid);
-  stg.load_v(vbase + elem * ES, min(BLK, Lk - key0), tid);
+  int key0 = 0;
+  size_t elem = 0;
+  if (n_list > 0) {  // an empty list touches no entry
+    locate(0, key0, elem);
+    stg.load_k(kbase + elem * ES, min(BLK, Lk - key0), tid);
+    stg.store_k(k_lds, tid);
+    stg.load_v(vbase + elem * ES, min(BLK, Lk - key0), tid);
+  }
 
   for (int t = 0; t < n_list; ++t) {
     int nkey0 = 0;

@@ -150,52 +150,57 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
   // ---- per-lane DMA source offsets (bytes within a page slab) ------------
   // Copy n of wave w fills LDS bytes [(w*NL + n) * 1024, +1024): row
   // r = (w*NL + n)*RPC + lane/CH, physical chunk lane%CH, which must hold the
-  // logical chunk (lane%CH) ^ swz(r). With NL a multiple of 4 (d = 128) the
-  // K swizzle depends on n mod 4 only; with RPC a multiple of CH (d = 64) on
-  // the lane only; the V swizzle depends on the lane only in both cases.
-  static_assert(D == 64 || NL % 4 == 0, "K swizzle period");
+  // logical chunk (lane%CH) ^ swz(r). With d = 128 (RPC = 4, CH = 16, NL a
+  // multiple of 4) the K swizzle of copy n is (lane%16) ^ (lane/16) ^ 4*(n%4),
+  // i.e. copy 0's offset with its chunk bits flipped by (n%4) << 6; with d = 64
+  // (RPC = CH = 8) it depends on the lane only. The V swizzle depends on the
+  // lane only in both cases.
+  static_assert(D == 64 || (RPC == 4 && CH == 16 && NL % 4 == 0), "K swizzle period");
   static_assert(D == 128 || RPC % CH == 0, "K swizzle period");
+  static_assert(NL == QREGS, "one V copy per k-step of S");
   const uint32_t dma_lane = (uint32_t)((lane / CH) * ROWB);
-  uint32_t dma_kx[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = u * RPC + lane / CH;  // a row with the same K swizzle as copy n = u (mod 4)
-    dma_kx[u] = dma_lane + (uint32_t)(((lane % CH) ^ Gm::swz_k(r)) * 16);
-  }
-  const uint32_t dma_vx = dma_lane + (uint32_t)(((lane % CH) ^ Gm::swz_v(lane / CH)) * 16);
-  // Copy the K (or V) tile of list entry t into LDS. Rows past the sequence
-  // end re-read the last valid row (their scores are masked). Returns kb.
-  auto dma_tile = [&](int t, bool is_k) -> int {
-    int kb = DENSE ? t : __builtin_amdgcn_readfirstlane(lst[t]);  // uniform: keeps the mask branch scalar
+  const uint32_t dma_k0 = dma_lane + (uint32_t)(((lane % CH) ^ Gm::swz_k(lane / CH)) * 16);
+  const uint32_t dma_v0 = dma_lane + (uint32_t)(((lane % CH) ^ Gm::swz_v(lane / CH)) * 16);
+  // ---- list walk --------------------------------------------------------------
+  // Entry t names block kb_t, whose page comes from the block table. Both loads
+  // for entry t+1 are issued a tile ahead (after barrier A of tile t) and read
+  // after barrier C, so their latency hides under the tile's work. An entry
+  // that is not a causal block of the row, or a page out of range, sets `bad`.
+  auto entry_at = [&](int t) -> int { return DENSE ? t : lst[t]; };
+  auto check_kb = [&](int raw) -> int {
+    int kb = __builtin_amdgcn_readfirstlane(raw);  // uniform: keeps the mask branch scalar
     if (kb < 0 || kb >= n_causal) {
       bad = 1;
       kb = 0;
     }
-    int page = __builtin_amdgcn_readfirstlane(table[kb]);
+    return kb;
+  };
+  auto check_page = [&](int raw) -> int {
+    int page = __builtin_amdgcn_readfirstlane(raw);
     if ((unsigned)page >= (unsigned)sq.num_pages) {
       bad = 1;
       page = 0;
     }
-    const int nvalid = min(BLK, Lk - kb * BLK);
-    const unsigned char* src = (is_k ? kglob : vglob) + (size_t)page * page_bytes;
-    unsigned char* dst = (is_k ? kbuf : vbuf) + w * NL * 1024;
-    if (nvalid >= BLK) {
-      const unsigned char* wsrc = src + (size_t)w * NL * 1024;
-#pragma unroll
-      for (int n = 0; n < NL; ++n) {
-        const uint32_t o = (is_k ? dma_kx[n % 4] : dma_vx) + (uint32_t)(n * 1024);
-        __builtin_amdgcn_global_load_lds((const void*)(wsrc + o), (lds_void*)(dst + n * 1024), 16, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int n = 0; n < NL; ++n) {
-        const int r = (w * NL + n) * RPC + lane / CH;
-        const int sw = is_k ? Gm::swz_k(r) : Gm::swz_v(r);
-        const uint32_t o = (uint32_t)(min(r, nvalid - 1) * ROWB + (((lane % CH) ^ sw) * 16));
-        __builtin_amdgcn_global_load_lds((const void*)(src + o), (lds_void*)(dst + n * 1024), 16, 0, 0);
-      }
-    }
-    return kb;
+    return page;
+  };
+  // A tile copy is issued as NL single-instruction copies that the loop spreads
+  // over the MFMA k-steps, so their issue cost hides under matrix work. A
+  // partial tile (the last block of a sequence) is copied whole from its page:
+  // key rows past the sequence end only ever meet the causal mask, which
+  // replaces their scores, and value rows past the end are zeroed in LDS before
+  // P.V reads them.
+  struct Copy {
+    const unsigned char* src;  // this wave's part of the page slab
+    unsigned char* dst;        // this wave's part of the LDS tile
+  };
+  auto copy_of = [&](int page, bool is_k) -> Copy {
+    return Copy{(is_k ? kglob : vglob) + (size_t)page * page_bytes + (size_t)w * NL * 1024,
+                (is_k ? kbuf : vbuf) + w * NL * 1024};
+  };
+  auto issue = [&](const Copy& c, bool is_k, int n) {
+    uint32_t o = (is_k ? dma_k0 ^ (D == 128 ? (uint32_t)((n & 3) << 6) : 0u) : dma_v0) + (uint32_t)(n * 1024);
+    asm volatile("" : "+v"(o));  // a fresh 32-bit lane offset: scalar base + vector offset addressing
+    __builtin_amdgcn_global_load_lds((const void*)(c.src + o), (lds_void*)(c.dst + n * 1024), 16, 0, 0);
   };
 
   // ---- operand addressing ---------------------------------------------------
@@ -226,11 +231,32 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
   int n_skip = 0;
   const float c2 = a.scale_log2;
 
-  int kb = dma_tile(0, true);  // K(0)
+  int kb = 0, page = 0;  // entry t
+  int raw_e = 0;         // entry t+1, loaded a tile ahead
+  Copy ck{}, cv{};
+  if (n_list > 0) {  // an empty list touches no entry
+    kb = check_kb(entry_at(0));
+    page = check_page(table[kb]);
+    ck = copy_of(page, true);
+#pragma unroll
+    for (int n = 0; n < NL; ++n) issue(ck, true, n);  // K(0)
+    raw_e = entry_at(min(1, n_list - 1));
+  }
+  bool pend = false;  // K(t) still to be issued: the previous block was skipped
   for (int t = 0; t < n_list; ++t) {
+    if (pend) {
+#pragma unroll 1
+      for (int n = 0; n < NL; ++n) issue(ck, true, n);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // A: K(t) landed; every wave is done with V(t-1)
-    dma_tile(t, false);  // V(t)
+    // entry t+1 (the last entry again after the end, which keeps the K copies
+    // of the next step unconditional) and its page; entry t+2
+    const int kb_next = check_kb(raw_e);
+    const int raw_p = table[kb_next];
+    raw_e = entry_at(min(t + 2, n_list - 1));
+    const int nvalid = min(BLK, Lk - kb * BLK);
+    cv = copy_of(page, false);  // V(t): copies issued during the S k-steps
 
     // ---- S^T = K Q^T for this wave's 32 rows -------------------------------
     // fragments of k-step ks+1 are read while the MFMAs of k-step ks run
@@ -245,6 +271,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
       for (int kt = 0; kt < KT; ++kt) kf[0][kt] = *(const bf16x8*)(k_lane + ((hl ^ k_swz) << 4) + kt * 32 * ROWB);
 #pragma unroll
       for (int ks = 0; ks < QREGS; ++ks) {
+        issue(cv, false, ks);  // one V copy per k-step
         if (ks + 1 < QREGS) {
           const unsigned char* kp = k_lane + (((2 * (ks + 1) + hl) ^ k_swz) << 4);
 #pragma unroll
@@ -254,10 +281,12 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
         for (int kt = 0; kt < KT; ++kt)
           s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks & 1][kt], qf[ks], s[kt], 0, 0, 0);
       }
-      // pin the order: the reads of step ks+1 are issued ahead of the MFMAs of step ks
+      // pin the order: per k-step, its V copies and the reads of step ks+1 are
+      // issued ahead of the MFMAs of step ks
       __builtin_amdgcn_sched_group_barrier(0x100, KT, 0);  // DS reads (step 0)
 #pragma unroll
       for (int ks = 0; ks < QREGS; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // copy
         if (ks + 1 < QREGS) __builtin_amdgcn_sched_group_barrier(0x100, KT, 0);  // DS reads (step ks+1)
         __builtin_amdgcn_sched_group_barrier(0x008, KT, 0);                       // MFMA (step ks)
       }
@@ -297,12 +326,20 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
         skip = __builtin_amdgcn_readfirstlane(worst < a.skip_thr_raw ? 1 : 0) != 0;
       }
     }
-    const int kb_next = (t + 1 < n_list) ? dma_tile(t + 1, true) : 0;  // K(t+1)
+    // K(t+1): copies issued during P.V (drained before exit)
+    const int page_next = check_page(raw_p);
+    ck = copy_of(page_next, true);
+    constexpr int KPS = (NL + 2 * KT - 1) / (2 * KT);  // K copies per P.V k-step
 
     // ---- online-softmax update and O^T += V^T P^T, one 32-key tile at a time:
     // the exps of tile kt+1 (VALU) run while the P.V MFMAs of tile kt execute
     n_skip += skip ? 1 : 0;
     if (!skip) {
+      if (nvalid < BLK) {  // zero the value rows past the sequence end
+        uint4* z = (uint4*)(vbuf + nvalid * ROWB);
+        for (int i = tid; i < (BLK - nvalid) * ROWB / 16; i += Gm::THREADS) z[i] = make_uint4(0, 0, 0, 0);
+        __syncthreads();
+      }
       const float m_new = fmaxf(m_run, m_loc);
       const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
       const float mc = (m_new == kNegInf) ? 0.f : m_new * c2;
@@ -340,6 +377,8 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int st = 2 * kt + s2;
+#pragma unroll
+          for (int n = st * KPS; n < (st + 1) * KPS && n < NL; ++n) issue(ck, true, n);
           if (st + 1 < 2 * KT)
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
@@ -356,12 +395,15 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
       }
       l_run = l_run * alpha + rs;
     }
+    pend = skip;
     if constexpr (!DENSE) {
       if (tid == 0 && a.skip_bits) a.skip_bits[out_row * a.kmax + t] = skip ? 1 : 0;
     }
     kb = kb_next;
+    page = page_next;
   }
 
+  __builtin_amdgcn_s_waitcnt(0);  // the trailing re-copy lands before the workgroup's LDS is released
   // ---- epilogue -------------------------------------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;

@@ -132,3 +132,55 @@ def test_kap_parity(run):
     assert np.array_equal(np.isfinite(P), fin), "visibility pattern of P"
     rel = 1e-2 if case.dtype == "bf16" else 1e-5
     assert np.abs(P[fin] - P64[fin]).max() <= rel * np.abs(P64[fin]).max()
+
+
+def test_empty_and_corrupt_lists(run):
+    """An empty list yields O = 0 and lse = -inf without reading any entry; an
+    entry that is not a causal block of its row makes that row NaN; every other
+    row is bit-identical to the run on the unmodified lists."""
+    case, dev = run["case"], run["dev"]
+    say(run["name"], "empty and corrupt lists")
+    order = run["ko"]["order"].copy()
+    count = run["ko"]["count"].copy()
+    lq0 = int(case.cu_seqlens_q[1] - case.cu_seqlens_q[0])
+    last_qb = (lq0 - 1) // case.block
+    g_last = case.h_kv - 1
+    # empty rows whose entries are garbage: must not be read
+    count[0, 0, 0] = 0
+    order[0, 0, 0, :] = 1 << 30
+    count[0, g_last, last_qb] = 0
+    order[0, g_last, last_qb, :] = -5
+    # a corrupt row (needs a second query block and a list of two entries)
+    corrupt = last_qb >= 1 and count[0, 0, last_qb] >= 2
+    if corrupt:  # the first block past the row's causal range
+        off = int(case.seqlens_k[0]) - lq0
+        order[0, 0, last_qb, 1] = (off + lq0 - 1) // case.block + 1
+    base = cosa.osk_attention(dev.problem, dev.q, dev.k, dev.v, run["order"], run["count"], case.tau,
+                              skip_bits=True, lse=True)
+    g = cosa.osk_attention(dev.problem, dev.q, dev.k, dev.v, torch.from_numpy(order).cuda(),
+                           torch.from_numpy(count).cuda(), case.tau, skip_bits=True, lse=True)
+    torch.cuda.synchronize()
+    grp = case.h_q // case.h_kv
+    B = case.block
+    O = g["O"].float().cpu().numpy()
+    O0 = base["O"].float().cpu().numpy()
+    lse, lse0 = g["lse"].cpu().numpy(), base["lse"].cpu().numpy()
+    touched = np.zeros(O.shape[:2], dtype=bool)  # [token, head]
+    for (gg, qb) in ((0, 0), (g_last, last_qb)):
+        rows = slice(qb * B, min(qb * B + B, lq0))
+        heads = slice(gg * grp, (gg + 1) * grp)
+        assert np.all(O[rows, heads] == 0.0)
+        assert np.all(lse[heads, rows] == -np.inf)
+        assert np.all(g["visited"].cpu().numpy()[0, heads, qb] == 0)
+        assert np.all(g["skipped"].cpu().numpy()[0, heads, qb] == 0)
+        assert np.all(g["skip_bits"].cpu().numpy()[0, heads, qb] == 255)
+        touched[rows, heads] = True
+    if corrupt:
+        rows = slice(last_qb * B, min(last_qb * B + B, lq0))
+        heads = slice(0, grp)
+        assert np.all(np.isnan(O[rows, heads]))
+        assert np.all(np.isnan(lse[heads, rows]))
+        touched[rows, heads] = True
+    keep = ~touched
+    assert np.array_equal(O[keep].view(np.uint32), O0[keep].view(np.uint32))
+    assert np.array_equal(lse.T[keep].view(np.uint32), lse0.T[keep].view(np.uint32))
