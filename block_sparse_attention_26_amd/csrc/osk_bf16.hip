@@ -38,6 +38,7 @@ namespace cosa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -45,13 +46,40 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// x combined with lane l ^ 32's x (v_permlane32_swap exchanges the halves)
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// max with a DPP-permuted copy of x (within rows of 16 lanes)
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float x) {
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false)));
+}
+
+// max of x over lanes 0..31, uniform: quad butterflies, half-row and row
+// mirrors, then the two 16-lane rows
 __device__ __forceinline__ float wave_max32(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 8));
-  x = fmaxf(x, __shfl_xor(x, 4));
-  x = fmaxf(x, __shfl_xor(x, 2));
-  x = fmaxf(x, __shfl_xor(x, 1));
-  return x;
+  x = dpp_max<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = dpp_max<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = dpp_max<0x141>(x);  // row_half_mirror
+  x = dpp_max<0x140>(x);  // row_mirror
+  return fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)),
+               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16)));
+}
+
+__device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// max of the 16 values of an accumulator, as a shallow tree
+__device__ __forceinline__ float max16(const f32x16& v) {
+  const float t0 = fmax3(v[0], v[1], v[2]), t1 = fmax3(v[3], v[4], v[5]), t2 = fmax3(v[6], v[7], v[8]);
+  const float t3 = fmax3(v[9], v[10], v[11]), t4 = fmax3(v[12], v[13], v[14]);
+  return fmaxf(fmax3(t0, t1, t2), fmax3(t3, t4, v[15]));
 }
 
 template <int D, int BLK>
@@ -302,12 +330,10 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
         for (int v = 0; v < 16; ++v)
           if (kt * 32 + 8 * (v >> 2) + (v & 3) > thr) s[kt][v] = kNegInf;
     }
-    float m_loc = kNegInf;
+    float m_loc = max16(s[0]);
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) m_loc = fmaxf(m_loc, s[kt][v]);
-    m_loc = fmaxf(m_loc, __shfl_xor(m_loc, 32));
+    for (int kt = 1; kt < KT; ++kt) m_loc = fmaxf(m_loc, max16(s[kt]));
+    m_loc = max_xor32(m_loc);
     if constexpr (!DENSE) {
       if (a.skip_on) {
         float diff = (row_valid && m_loc != kNegInf) ? m_loc - m_run : kNegInf;
@@ -351,13 +377,25 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
       }
       m_run = m_new;
       float rs = 0.f;
+      // P tile kt in bf16; the row sum adds the same rounded weights that
+      // enter P.V, two per bf16 dot product, in a chain per tile
+      const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
       auto ptile = [&](int kt, bf16x8 (&pd)[2]) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][v], c2, -mc));
-          rs += p;
-          pd[v >> 3][v & 7] = (__bf16)p;
-        }
+        for (int v = 0; v < 16; ++v)
+          pd[v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][v], c2, -mc));
+        // (pairs taken with constant shuffles: extracting them through a
+        // bit cast to 32-bit lanes is miscompiled by this toolchain)
+        float r = 0.f;
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pd[0], pd[0], 0, 1), ones, r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pd[0], pd[0], 2, 3), ones, r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pd[0], pd[0], 4, 5), ones, r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pd[0], pd[0], 6, 7), ones, r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pd[1], pd[1], 0, 1), ones, r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pd[1], pd[1], 2, 3), ones, r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pd[1], pd[1], 4, 5), ones, r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pd[1], pd[1], 6, 7), ones, r, false);
+        rs += r;
       };
       auto vread = [&](int st, int dt, int e) -> s16x4 {
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -405,7 +443,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
 
   __builtin_amdgcn_s_waitcnt(0);  // the trailing re-copy lands before the workgroup's LDS is released
   // ---- epilogue -------------------------------------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_xor32(l_run);
   float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (bad) inv = __builtin_nanf("");
   if (row_valid) {
