@@ -140,7 +140,7 @@ constexpr int kScoreKeys = 128;
 
 template <bool BF16, int D, int BLK>
 __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
-  __shared__ float tile[kScoreRows][kScoreKeys + 1];
+  __shared__ float tile[2][kScoreRows][kScoreKeys + 1];  // double-buffered: one barrier per step
   const SeqArgs& sq = a.seq;
   const int G = sq.group;
   const int ntile = (a.max_nr + kScoreRows - 1) / kScoreRows;
@@ -203,40 +203,98 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
   }
 
   const int jend = kb_end * per;  // pooled keys covered
-  for (int j0 = 0; j0 < jend; j0 += kScoreKeys) {
-    // ---- one 32x32 MFMA tile per wave: keys j0 + w*32 + [0,32) ----------
-    const int jk = j0 + w * 32 + l32;  // the key row this lane loads (A operand)
-    const bool k_ok = jk < Rk && jk < jend;
-    size_t koff = 0;
-    if (k_ok) {
-      const int kbk = jk / per;
-      const int page = sq.block_table[(int64_t)b * sq.max_blocks_k + kbk];
-      koff = ((((size_t)page * sq.h_kv + g) * per) + jk % per) * D;
-    }
-    f32x16 s;
+  const bool reg_max = per >= 4 && per <= 32;  // else the step goes through LDS
+  // this lane's key row (A operand) of the step at j0: element offset, or -1
+  auto key_off = [&](int j0) -> int64_t {
+    const int jk = j0 + w * 32 + l32;
+    if (!(jk < Rk && jk < jend)) return -1;
+    const int kbk = jk / per;
+    const int page = sq.block_table[(int64_t)b * sq.max_blocks_k + kbk];
+    return (int64_t)((((size_t)page * sq.h_kv + g) * per) + jk % per) * D;
+  };
+  // the next step's K fragments are loaded while the current step computes
+  constexpr int KREGS = BF16 ? QREGS : 1;
+  uint4 kc[KREGS], kn[KREGS];
+  int64_t koff_c = key_off(0);
+  if constexpr (BF16) {
+    const uint16_t* kp = (const uint16_t*)a.k_pool + (koff_c < 0 ? 0 : koff_c) + hl * 8;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = 0.f;
+    for (int ks = 0; ks < QREGS; ++ks) kc[ks] = koff_c >= 0 ? *(const uint4*)(kp + ks * 16) : make_uint4(0, 0, 0, 0);
+  }
+  int it = 0;
+  for (int j0 = 0; j0 < jend; j0 += kScoreKeys, ++it) {
+    const int64_t koff_n = j0 + kScoreKeys < jend ? key_off(j0 + kScoreKeys) : -1;
     if constexpr (BF16) {
-      const uint16_t* kp = (const uint16_t*)a.k_pool + koff + hl * 8;
+      const uint16_t* kp = (const uint16_t*)a.k_pool + (koff_n < 0 ? 0 : koff_n) + hl * 8;
 #pragma unroll
-      for (int ks = 0; ks < QREGS; ++ks) {
-        uint4 x = k_ok ? *(const uint4*)(kp + ks * 16) : make_uint4(0, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), qf16[ks], s, 0, 0, 0);
-      }
-    } else {
-      const float* kp = (const float*)a.k_pool + koff + hl;
+      for (int ks = 0; ks < QREGS; ++ks) kn[ks] = koff_n >= 0 ? *(const uint4*)(kp + ks * 16) : make_uint4(0, 0, 0, 0);
+    }
+    // ---- one 32x32 MFMA tile per wave: keys j0 + w*32 + [0,32) ----------
+    f32x16 sc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+    if constexpr (BF16) {
 #pragma unroll
       for (int ks = 0; ks < QREGS; ++ks)
-        s = __builtin_amdgcn_mfma_f32_32x32x2f32(k_ok ? kp[2 * ks] : 0.f, qf32[ks], s, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kc[ks]), qf16[ks], sc, 0, 0, 0);
+    } else {
+      const bool k_ok = koff_c >= 0;
+      const float* kp = (const float*)a.k_pool + (k_ok ? koff_c : 0) + hl;
+#pragma unroll
+      for (int ks = 0; ks < QREGS; ++ks)
+        sc = __builtin_amdgcn_mfma_f32_32x32x2f32(k_ok ? kp[2 * ks] : 0.f, qf32[ks], sc, 0, 0, 0);
     }
-    __syncthreads();  // previous step's tile fully consumed
+    // element v of this lane: key jj = w*32 + 8*(v/4) + 4*hl + v%4 of the step
+    float x[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int jj = w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3);  // key within the step
-      const int j = j0 + jj;
-      const float x = (j <= my_jmax && j < Rk) ? s[v] * a.scale : kNegInf;
-      tile[l32][jj] = x;
+      const int j = j0 + w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3);
+      x[v] = (j <= my_jmax && j < Rk) ? sc[v] * a.scale : kNegInf;
     }
+    if (reg_max) {
+      // blocks of 4..32 keys lie inside one wave's 32 keys: maxima in
+      // registers, the two lane halves exchanged with v_permlane32_swap
+      float g4[4], o4[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) g4[q] = fmaxf(fmaxf(x[4 * q], x[4 * q + 1]), fmaxf(x[4 * q + 2], x[4 * q + 3]));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(g4[q]), __float_as_uint(g4[q]), false, false);
+        o4[q] = __uint_as_float(hl ? sw[0] : sw[1]);  // the other half's value
+      }
+      const int r = r0 + l32;
+      if (hl == 0 && r < R) {
+        float* prow = P + (int64_t)r * sq.max_nk;
+        const int kbase = (j0 + w * 32) / per;
+        float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        int nb;
+        if (per == 4) {  // block 2q + half
+          nb = 8;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            m[2 * q] = g4[q];
+            m[2 * q + 1] = o4[q];
+          }
+        } else if (per == 8) {  // block q
+          nb = 4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) m[q] = fmaxf(g4[q], o4[q]);
+        } else if (per == 16) {  // block q/2
+          nb = 2;
+          m[0] = fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1]));
+          m[1] = fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3]));
+        } else {  // per == 32
+          nb = 1;
+          m[0] = fmaxf(fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1])), fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3])));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i < nb && kbase + i < kb_end) prow[kbase + i] = m[i];
+      }
+    } else {
+    float (*tl)[kScoreKeys + 1] = tile[it & 1];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tl[l32][w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3)] = x[v];
     __syncthreads();
     // ---- per-block maxima of the 128-key step ------------------------------
     const int nblk = kScoreKeys / per < 1 ? 1 : kScoreKeys / per;
@@ -246,9 +304,15 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
       const int r = r0 + rr;
       if (r >= R || kb >= kb_end) continue;
       float m = kNegInf;
-      for (int e = 0; e < per; ++e) m = fmaxf(m, tile[rr][bi * per + e]);
+      for (int e = 0; e < per; ++e) m = fmaxf(m, tl[rr][bi * per + e]);
       P[(int64_t)r * sq.max_nk + kb] = m;
     }
+    }
+    if constexpr (BF16) {
+#pragma unroll
+      for (int ks = 0; ks < QREGS; ++ks) kc[ks] = kn[ks];
+    }
+    koff_c = koff_n;
   }
   if (a.fill_scores) {
     // -inf for blocks past this tile's reach and for padding rows
@@ -328,7 +392,12 @@ __global__ __launch_bounds__(kThreads) void kap_rank_sort(KapArgs a) {
     const int h = g * G + ri / nrow, r = r0 + ri % nrow;
     const float* row = Pb + ((int64_t)h * a.max_nr + r) * sq.max_nk;
     float m = kNegInf;
-    for (int kb = lane; kb < n; kb += 64) m = fmaxf(m, row[kb]);
+    int kb = lane;
+    for (; kb + 192 < n; kb += 256) {  // four independent loads in flight
+      const float x0 = row[kb], x1 = row[kb + 64], x2 = row[kb + 128], x3 = row[kb + 192];
+      m = fmaxf(m, fmaxf(fmaxf(x0, x1), fmaxf(x2, x3)));
+    }
+    for (; kb < n; kb += 64) m = fmaxf(m, row[kb]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
     if (lane == 0) rmax[ri] = m;
@@ -342,16 +411,32 @@ __global__ __launch_bounds__(kThreads) void kap_rank_sort(KapArgs a) {
     if (kb < n) {
       float s = 0.0f;
       bool flag = false;
-      for (int ri = 0; ri < NR; ++ri) {  // heads ascending, then rows ascending
-        const int h = g * G + ri / nrow, r = r0 + ri % nrow;
-        const float x = Pb[((int64_t)h * a.max_nr + r) * sq.max_nk + kb];
-        float dlt;
-        {
-#pragma clang fp contract(off)
-          dlt = x - rmax[ri];
-          s = s + exp32(dlt);
+      // heads ascending, then rows ascending; the loads of a chunk of rows are
+      // issued together, the sum stays sequential
+      constexpr int CHUNK = 8;
+      for (int r0c = 0; r0c < NR; r0c += CHUNK) {
+        float xs[CHUNK];
+#pragma unroll
+        for (int c = 0; c < CHUNK; ++c) {
+          const int ri = r0c + c;
+          if (ri < NR) {
+            const int h = g * G + ri / nrow, r = r0 + ri % nrow;
+            xs[c] = Pb[((int64_t)h * a.max_nr + r) * sq.max_nk + kb];
+          }
         }
-        flag |= (dlt == 0.0f);
+#pragma unroll
+        for (int c = 0; c < CHUNK; ++c) {
+          const int ri = r0c + c;
+          if (ri < NR) {
+            float dlt;
+            {
+#pragma clang fp contract(off)
+              dlt = xs[c] - rmax[ri];
+              s = s + exp32(dlt);
+            }
+            flag |= (dlt == 0.0f);
+          }
+        }
       }
       key = ((unsigned long long)(flag ? 1u : 0u) << 63) |
             ((unsigned long long)__builtin_bit_cast(uint32_t, s) << 32) |

@@ -43,6 +43,11 @@ CASES = {
     "bf16-d128-b64": _lr("bf16-d128-b64", 18, [1300], [1400], hq=4, hkv=4, d=128, B=64, p=4),
     "bf16-d64-b64-sinks": _lr("bf16-d64-b64-sinks", 19, [1100], hq=4, hkv=2, d=64, B=64, p=64,
                               sink_logit=26.0),
+    # pooled keys per block (B/p) of 4, 32, 2 and 128: every block-max path of the proxy
+    "bf16-b128-p32": _lr("bf16-b128-p32", 20, [900], hq=4, hkv=2, d=128, B=128, p=32),
+    "bf16-b128-p4": _lr("bf16-b128-p4", 21, [800], [1000], hq=4, hkv=2, d=128, B=128, p=4),
+    "bf16-b64-p32": _lr("bf16-b64-p32", 22, [700], hq=2, hkv=1, d=64, B=64, p=32),
+    "bf16-b128-p1": _lr("bf16-b128-p1", 23, [600], hq=2, hkv=2, d=64, B=128, p=1),
 }
 
 
