@@ -110,6 +110,7 @@ size_t kap_ws_size(const cosa_problem* p, int pool, bool with_scores) {
   const size_t es = p->dtype == COSA_BF16 ? 2 : 4;
   size_t sz = align256((size_t)p->batch * d.max_nr * p->h_q * p->head_dim * es);
   sz += align256((size_t)p->num_pages * p->h_kv * (p->block / pool) * p->head_dim * es);
+  sz += align256((size_t)p->batch * p->h_q * d.max_nr * sizeof(float));  // row maxima of P
   if (with_scores) sz += align256((size_t)p->batch * p->h_q * d.max_nr * d.max_nk * sizeof(float));
   return sz;
 }
@@ -242,6 +243,11 @@ cosa_status cosa_kap_order(const cosa_problem* problem, const void* q, const voi
   a.k_pool = ws;
   ws += align256((size_t)problem->num_pages * problem->h_kv * (problem->block / pool) *
                  problem->head_dim * es);
+  // the score pass reduces rows of P to their maxima when blocks hold 4..32
+  // pooled keys; otherwise the rank pass does
+  const int per = problem->block / pool;
+  a.row_max = (per >= 4 && per <= 32) ? (float*)ws : nullptr;
+  ws += align256((size_t)problem->batch * problem->h_q * d.max_nr * sizeof(float));
   a.scores = own_scores ? (float*)ws : proxy_scores;
   a.fill_scores = own_scores ? 0 : 1;
   a.block_scores = block_scores;

@@ -14,6 +14,10 @@ constexpr int kNumXcd = 8;
 // Largest KV-block count per sequence the proxy's in-LDS sort handles.
 constexpr int kMaxSortBlocks = 4096;
 
+// Longest list the two-head attention kernel stages in LDS (longer lists, or
+// a dense walk over more blocks, take the single-head kernel).
+constexpr int kMaxDbList = 4096;
+
 struct SeqArgs {
   const int32_t* cu_seqlens_q;  // [batch+1]
   const int32_t* seqlens_k;     // [batch]
@@ -54,6 +58,7 @@ struct KapArgs {
   float* scores;         // P: [batch, h_q, max_nr, max_nk] fp32
   int32_t fill_scores;   // 1: write -inf into every non-visible entry of P
   float* block_scores;   // nullable [batch, h_kv, max_nq, max_nk]
+  float* row_max;        // nullable [batch, h_q, max_nr]: row maxima of P from the score pass
   int32_t* order;        // [batch, h_kv, max_nq, kmax]
   uint8_t* hrm;          // [batch, h_kv, max_nq, kmax]
   int32_t* count;        // [batch, h_kv, max_nq]

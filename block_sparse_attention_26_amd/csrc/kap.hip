@@ -131,19 +131,23 @@ __global__ __launch_bounds__(kThreads) void kap_pool_k(KapArgs a) {
 }
 
 // ---- proxy scores with fused MaxPool (readings R2-R4) ----------------------
-// One workgroup per (sequence, query head, tile of 32 pooled rows), longest
-// tiles first. Each of the 4 waves computes a 32-key x 32-row tile of
-// S^T = Kpool . Qpool^T per step (128 pooled keys per step); the tile goes
-// through LDS and the workgroup reduces it to per-KV-block maxima.
+// One workgroup per (sequence, query head, tile of 32*RT pooled rows), longest
+// tiles first. Each of the 4 waves computes 32-key x 32-row tiles of
+// S^T = Kpool . Qpool^T per step (128 pooled keys per step), one per row tile
+// against the same K fragments (loaded one step ahead). Blocks of 4..32 pooled
+// keys are reduced to their maxima in registers (RT = 2); other block sizes go
+// through LDS (RT = 1).
 constexpr int kScoreRows = 32;
 constexpr int kScoreKeys = 128;
 
-template <bool BF16, int D, int BLK>
+template <bool BF16, int D, int BLK, int RT>
 __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
-  __shared__ float tile[2][kScoreRows][kScoreKeys + 1];  // double-buffered: one barrier per step
+  constexpr int ROWS = kScoreRows * RT;  // pooled query rows per workgroup
+  // LDS reduction (blocks of 1, 2, 64 or 128 pooled keys), double-buffered
+  __shared__ float tile[RT == 1 ? 2 : 1][RT == 1 ? kScoreRows : 1][kScoreKeys + 1];
   const SeqArgs& sq = a.seq;
   const int G = sq.group;
-  const int ntile = (a.max_nr + kScoreRows - 1) / kScoreRows;
+  const int ntile = (a.max_nr + ROWS - 1) / ROWS;
   const int64_t bid = blockIdx.x;
   const int h = (int)(bid % sq.h_q);
   int64_t rest = bid / sq.h_q;
@@ -159,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
   const int R = (Lq + p - 1) / p;
   const int Rk = (Lk + p - 1) / p;
   const int nk = (Lk + BLK - 1) / BLK;
-  const int r0 = rt * kScoreRows;
+  const int r0 = rt * ROWS;
   float* P = a.scores + (((int64_t)b * sq.h_q + h) * a.max_nr) * sq.max_nk;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
 
   if (r0 >= R) {
     if (a.fill_scores)
-      for (int i = tid; i < kScoreRows * sq.max_nk; i += kThreads) {
+      for (int i = tid; i < ROWS * sq.max_nk; i += kThreads) {
         const int r = r0 + i / sq.max_nk;
         if (r < a.max_nr) P[(int64_t)r * sq.max_nk + i % sq.max_nk] = kNegInf;
       }
@@ -175,35 +179,36 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
   }
   // Blocks computed: every causal block of the query block holding the
   // tile's last row (a superset of what any row of the tile can see).
-  const int r_last = min(r0 + kScoreRows, R) - 1;
+  const int r_last = min(r0 + ROWS, R) - 1;
   const int qb_last = r_last / per;
   const int kb_end = min((off + min(qb_last * BLK + BLK - 1, Lq - 1)) / BLK + 1, nk);
 
-  // this lane's query row (B operand)
-  const int my_r = r0 + l32;
-  const bool r_ok = my_r < R;
-  const int my_jmax = r_ok ? (off + min(my_r * p + p - 1, Lq - 1)) / p : -1;
+  // this lane's query rows (B operands), one per row tile
+  int my_jmax[RT];
   constexpr int QREGS = BF16 ? D / 16 : D / 2;
-  bf16x8 qf16[BF16 ? QREGS : 1];
-  float qf32[BF16 ? 1 : QREGS];
-  {
+  bf16x8 qf16[RT][BF16 ? QREGS : 1];
+  float qf32[RT][BF16 ? 1 : QREGS];
+#pragma unroll
+  for (int u = 0; u < RT; ++u) {
+    const int my_r = r0 + u * kScoreRows + l32;
+    const bool r_ok = my_r < R;
+    my_jmax[u] = r_ok ? (off + min(my_r * p + p - 1, Lq - 1)) / p : -1;
     const size_t qoff = (((size_t)b * a.max_nr + (r_ok ? my_r : r0)) * sq.h_q + h) * D;
     if constexpr (BF16) {
       const uint16_t* qp = (const uint16_t*)a.q_pool + qoff + hl * 8;
 #pragma unroll
       for (int ks = 0; ks < QREGS; ++ks) {
         uint4 x = r_ok ? *(const uint4*)(qp + ks * 16) : make_uint4(0, 0, 0, 0);
-        qf16[ks] = __builtin_bit_cast(bf16x8, x);
+        qf16[u][ks] = __builtin_bit_cast(bf16x8, x);
       }
     } else {
       const float* qp = (const float*)a.q_pool + qoff + hl;
 #pragma unroll
-      for (int ks = 0; ks < QREGS; ++ks) qf32[ks] = r_ok ? qp[2 * ks] : 0.f;
+      for (int ks = 0; ks < QREGS; ++ks) qf32[u][ks] = r_ok ? qp[2 * ks] : 0.f;
     }
   }
 
   const int jend = kb_end * per;  // pooled keys covered
-  const bool reg_max = per >= 4 && per <= 32;  // else the step goes through LDS
   // this lane's key row (A operand) of the step at j0: element offset, or -1
   auto key_off = [&](int j0) -> int64_t {
     const int jk = j0 + w * 32 + l32;
@@ -221,6 +226,9 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
 #pragma unroll
     for (int ks = 0; ks < QREGS; ++ks) kc[ks] = koff_c >= 0 ? *(const uint4*)(kp + ks * 16) : make_uint4(0, 0, 0, 0);
   }
+  float rmx[RT];  // running row maxima over this wave's keys (RT > 1)
+#pragma unroll
+  for (int u = 0; u < RT; ++u) rmx[u] = kNegInf;
   int it = 0;
   for (int j0 = 0; j0 < jend; j0 += kScoreKeys, ++it) {
     const int64_t koff_n = j0 + kScoreKeys < jend ? key_off(j0 + kScoreKeys) : -1;
@@ -229,84 +237,97 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
 #pragma unroll
       for (int ks = 0; ks < QREGS; ++ks) kn[ks] = koff_n >= 0 ? *(const uint4*)(kp + ks * 16) : make_uint4(0, 0, 0, 0);
     }
-    // ---- one 32x32 MFMA tile per wave: keys j0 + w*32 + [0,32) ----------
-    f32x16 sc;
+    // ---- per row tile, one 32x32 MFMA tile per wave: keys j0 + w*32 + [0,32)
+    f32x16 sc[RT];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+    for (int u = 0; u < RT; ++u)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sc[u][v] = 0.f;
     if constexpr (BF16) {
 #pragma unroll
       for (int ks = 0; ks < QREGS; ++ks)
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kc[ks]), qf16[ks], sc, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < RT; ++u)
+          sc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kc[ks]), qf16[u][ks], sc[u], 0, 0, 0);
     } else {
       const bool k_ok = koff_c >= 0;
       const float* kp = (const float*)a.k_pool + (k_ok ? koff_c : 0) + hl;
 #pragma unroll
-      for (int ks = 0; ks < QREGS; ++ks)
-        sc = __builtin_amdgcn_mfma_f32_32x32x2f32(k_ok ? kp[2 * ks] : 0.f, qf32[ks], sc, 0, 0, 0);
-    }
-    // element v of this lane: key jj = w*32 + 8*(v/4) + 4*hl + v%4 of the step
-    float x[16];
+      for (int ks = 0; ks < QREGS; ++ks) {
+        const float kv = k_ok ? kp[2 * ks] : 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int j = j0 + w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3);
-      x[v] = (j <= my_jmax && j < Rk) ? sc[v] * a.scale : kNegInf;
-    }
-    if (reg_max) {
-      // blocks of 4..32 keys lie inside one wave's 32 keys: maxima in
-      // registers, the two lane halves exchanged with v_permlane32_swap
-      float g4[4], o4[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) g4[q] = fmaxf(fmaxf(x[4 * q], x[4 * q + 1]), fmaxf(x[4 * q + 2], x[4 * q + 3]));
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(g4[q]), __float_as_uint(g4[q]), false, false);
-        o4[q] = __uint_as_float(hl ? sw[0] : sw[1]);  // the other half's value
+        for (int u = 0; u < RT; ++u) sc[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv, qf32[u][ks], sc[u], 0, 0, 0);
       }
-      const int r = r0 + l32;
-      if (hl == 0 && r < R) {
-        float* prow = P + (int64_t)r * sq.max_nk;
-        const int kbase = (j0 + w * 32) / per;
-        float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        int nb;
-        if (per == 4) {  // block 2q + half
-          nb = 8;
+    }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            m[2 * q] = g4[q];
-            m[2 * q + 1] = o4[q];
-          }
-        } else if (per == 8) {  // block q
-          nb = 4;
+    for (int u = 0; u < RT; ++u) {
+      // element v of this lane: key jj = w*32 + 8*(v/4) + 4*hl + v%4 of the step
+      float x[16];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) m[q] = fmaxf(g4[q], o4[q]);
-        } else if (per == 16) {  // block q/2
-          nb = 2;
-          m[0] = fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1]));
-          m[1] = fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3]));
-        } else {  // per == 32
-          nb = 1;
-          m[0] = fmaxf(fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1])), fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3])));
+      for (int v = 0; v < 16; ++v) {
+        const int j = j0 + w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3);
+        x[v] = (j <= my_jmax[u] && j < Rk) ? sc[u][v] * a.scale : kNegInf;
+      }
+      if constexpr (RT > 1) {
+        // blocks of 4..32 keys lie inside one wave's 32 keys: maxima in
+        // registers, the two lane halves exchanged with v_permlane32_swap
+        float g4[4], o4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) g4[q] = fmaxf(fmaxf(x[4 * q], x[4 * q + 1]), fmaxf(x[4 * q + 2], x[4 * q + 3]));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(g4[q]), __float_as_uint(g4[q]), false, false);
+          o4[q] = __uint_as_float(hl ? sw[0] : sw[1]);  // the other half's value
         }
+        const int r = r0 + u * kScoreRows + l32;
+        rmx[u] = fmaxf(rmx[u], fmaxf(fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1])),
+                                     fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3]))));
+        if (hl == 0 && r < R) {
+          float* prow = P + (int64_t)r * sq.max_nk;
+          const int kbase = (j0 + w * 32) / per;
+          float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+          int nb;
+          if (per == 4) {  // block 2q + half
+            nb = 8;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (i < nb && kbase + i < kb_end) prow[kbase + i] = m[i];
+            for (int q = 0; q < 4; ++q) {
+              m[2 * q] = g4[q];
+              m[2 * q + 1] = o4[q];
+            }
+          } else if (per == 8) {  // block q
+            nb = 4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) m[q] = fmaxf(g4[q], o4[q]);
+          } else if (per == 16) {  // block q/2
+            nb = 2;
+            m[0] = fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1]));
+            m[1] = fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3]));
+          } else {  // per == 32
+            nb = 1;
+            m[0] = fmaxf(fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1])),
+                         fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3])));
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (i < nb && kbase + i < kb_end) prow[kbase + i] = m[i];
+        }
+      } else {
+        float (*tl)[kScoreKeys + 1] = tile[it & 1];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tl[l32][w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3)] = x[v];
+        __syncthreads();
+        // ---- per-block maxima of the 128-key step --------------------------
+        const int nblk = kScoreKeys / per < 1 ? 1 : kScoreKeys / per;
+        for (int i = tid; i < kScoreRows * nblk; i += kThreads) {
+          const int rr = i / nblk, bi = i % nblk;
+          const int kb = (j0 + bi * per) / per;
+          const int r = r0 + rr;
+          if (r >= R || kb >= kb_end) continue;
+          float m = kNegInf;
+          for (int e = 0; e < per; ++e) m = fmaxf(m, tl[rr][bi * per + e]);
+          P[(int64_t)r * sq.max_nk + kb] = m;
+        }
       }
-    } else {
-    float (*tl)[kScoreKeys + 1] = tile[it & 1];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) tl[l32][w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3)] = x[v];
-    __syncthreads();
-    // ---- per-block maxima of the 128-key step ------------------------------
-    const int nblk = kScoreKeys / per < 1 ? 1 : kScoreKeys / per;
-    for (int i = tid; i < kScoreRows * nblk; i += kThreads) {
-      const int rr = i / nblk, bi = i % nblk;
-      const int kb = (j0 + bi * per) / per;
-      const int r = r0 + rr;
-      if (r >= R || kb >= kb_end) continue;
-      float m = kNegInf;
-      for (int e = 0; e < per; ++e) m = fmaxf(m, tl[rr][bi * per + e]);
-      P[(int64_t)r * sq.max_nk + kb] = m;
-    }
     }
     if constexpr (BF16) {
 #pragma unroll
@@ -314,9 +335,29 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
     }
     koff_c = koff_n;
   }
+  if constexpr (RT > 1) {
+    // Row maxima of P: each wave saw a quarter of every step's keys, so the
+    // four partial maxima are combined through LDS. Blocks past a row's causal
+    // range are all -inf for that row, so the maximum equals the one over its
+    // causal blocks.
+    if (a.row_max) {
+      __shared__ float part[kThreads / 64][ROWS];
+      if (hl == 0)
+#pragma unroll
+        for (int u = 0; u < RT; ++u) part[w][u * kScoreRows + l32] = rmx[u];
+      __syncthreads();
+      for (int i = tid; i < ROWS; i += kThreads) {
+        const int r = r0 + i;
+        float m = part[0][i];
+#pragma unroll
+        for (int ww = 1; ww < kThreads / 64; ++ww) m = fmaxf(m, part[ww][i]);
+        if (r < R) a.row_max[((int64_t)b * sq.h_q + h) * a.max_nr + r] = m;
+      }
+    }
+  }
   if (a.fill_scores) {
     // -inf for blocks past this tile's reach and for padding rows
-    for (int i = tid; i < kScoreRows * sq.max_nk; i += kThreads) {
+    for (int i = tid; i < ROWS * sq.max_nk; i += kThreads) {
       const int r = r0 + i / sq.max_nk, kb = i % sq.max_nk;
       if (r >= a.max_nr) continue;
       if (r >= R || kb >= kb_end) P[(int64_t)r * sq.max_nk + kb] = kNegInf;
@@ -387,7 +428,14 @@ __global__ __launch_bounds__(kThreads) void kap_rank_sort(KapArgs a) {
   const int NR = G * nrow;
   const float* Pb = a.scores + ((int64_t)b * sq.h_q) * a.max_nr * sq.max_nk;
 
-  // row maxima over the row's causal blocks (max is exact in any order)
+  // row maxima over the row's causal blocks (max is exact in any order):
+  // from the score pass when it produced them
+  if (a.row_max) {
+    for (int ri = tid; ri < NR; ri += kThreads) {
+      const int h = g * G + ri / nrow, r = r0 + ri % nrow;
+      rmax[ri] = a.row_max[((int64_t)b * sq.h_q + h) * a.max_nr + r];
+    }
+  } else
   for (int ri = w; ri < NR; ri += kThreads / 64) {
     const int h = g * G + ri / nrow, r = r0 + ri % nrow;
     const float* row = Pb + ((int64_t)h * a.max_nr + r) * sq.max_nk;
@@ -492,9 +540,16 @@ hipError_t launch_all(const KapArgs& a, hipStream_t stream) {
   const int64_t g2 = (int64_t)sq.batch * sq.max_nk;
   hipLaunchKernelGGL((kap_pool_k<BF16, D, BLK>), dim3((unsigned)g2), dim3(kThreads), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t ntile = (a.max_nr + kScoreRows - 1) / kScoreRows;
-  const int64_t g3 = ntile * sq.batch * sq.h_q;
-  hipLaunchKernelGGL((kap_score<BF16, D, BLK>), dim3((unsigned)g3), dim3(kThreads), 0, stream, a);
+  const int per = BLK / a.pool;
+  if (per >= 4 && per <= 32) {  // block maxima in registers: two row tiles share each K load
+    const int64_t ntile = (a.max_nr + 2 * kScoreRows - 1) / (2 * kScoreRows);
+    const int64_t g3 = ntile * sq.batch * sq.h_q;
+    hipLaunchKernelGGL((kap_score<BF16, D, BLK, 2>), dim3((unsigned)g3), dim3(kThreads), 0, stream, a);
+  } else {
+    const int64_t ntile = (a.max_nr + kScoreRows - 1) / kScoreRows;
+    const int64_t g3 = ntile * sq.batch * sq.h_q;
+    hipLaunchKernelGGL((kap_score<BF16, D, BLK, 1>), dim3((unsigned)g3), dim3(kThreads), 0, stream, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t g4 = (int64_t)sq.max_nq * sq.batch * sq.h_kv;
   hipLaunchKernelGGL((kap_rank_sort<BLK>), dim3((unsigned)g4), dim3(kThreads), 0, stream, a);

@@ -102,8 +102,8 @@ def test_workspace_size_and_argument_errors():
     p = _problem((2048,))
     with_scores = cosa.cosa_kap_workspace_size(p.c, 16, True)
     without = cosa.cosa_kap_workspace_size(p.c, 16, False)
-    # pooled Q (16 rows x 32 heads x 128 x 2B per 256 tokens), pooled K, and P
-    assert without == 128 * 32 * 128 * 2 + 16 * 8 * 8 * 128 * 2
+    # pooled Q (16 rows x 32 heads x 128 x 2B per 256 tokens), pooled K, row maxima, and P
+    assert without == 128 * 32 * 128 * 2 + 16 * 8 * 8 * 128 * 2 + 32 * 128 * 4
     assert with_scores == without + 32 * 128 * 16 * 4
     assert cosa.cosa_kap_workspace_size(p.c, 3, True) == 0  # pool must divide block
     buf = FakeDev(1, 16)
