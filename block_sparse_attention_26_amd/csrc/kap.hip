@@ -461,7 +461,7 @@ __global__ __launch_bounds__(kThreads) void kap_rank_sort(KapArgs a) {
       bool flag = false;
       // heads ascending, then rows ascending; the loads of a chunk of rows are
       // issued together, the sum stays sequential
-      constexpr int CHUNK = 8;
+      constexpr int CHUNK = 16;
       for (int r0c = 0; r0c < NR; r0c += CHUNK) {
         float xs[CHUNK];
 #pragma unroll
