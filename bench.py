@@ -296,7 +296,7 @@ def main():
         "visited_head_blocks": visited,
         "skipped_head_blocks": skipped,
         "roofline": {
-            "kernel": "osk_kernel (ordered-skip walk)",
+            "kernel": "osk_bf16_kernel<128,128> (ordered-skip walk)",
             "bound": "mfma",
             "achieved": osk_tflops,
             "peak": peak,
