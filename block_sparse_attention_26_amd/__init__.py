@@ -6,11 +6,14 @@ There is no fallback: if the library is missing or fails to load, every entry
 point raises.
 
 Low-level functions carry the C names (``cosa_kap_order``,
-``cosa_osk_attention``, ``cosa_dense_attention``, ``cosa_validate``,
+``cosa_osk_attention``, ``cosa_dense_attention``, ``cosa_mask_from_order``,
+``cosa_order_from_mask``, ``cosa_osk_attention_masked``, ``cosa_block_mass``,
+``cosa_validate``,
 ``cosa_dims``, ``cosa_kap_workspace_size``) and take integer device pointers.
 The ``Problem`` class and the ``kap_order`` / ``osk_attention`` /
-``dense_attention`` helpers accept torch tensors that already live on the GPU
-and allocate the outputs with torch.
+``dense_attention`` / ``mask_from_order`` / ``order_from_mask`` /
+``osk_attention_masked`` / ``block_mass`` helpers accept torch tensors that already live on the
+GPU and allocate the outputs with torch.
 """
 from __future__ import annotations
 
@@ -23,8 +26,10 @@ __all__ = [
     "CosaError", "Problem", "load", "library_path",
     "cosa_validate", "cosa_dims", "cosa_kap_workspace_size", "cosa_kap_order",
     "cosa_osk_attention", "cosa_dense_attention", "cosa_status_string",
-    "cosa_last_error", "cosa_version",
-    "kap_order", "osk_attention", "dense_attention",
+    "cosa_last_error", "cosa_version", "cosa_mask_from_order", "cosa_order_from_mask",
+    "cosa_osk_attention_masked", "cosa_block_mass",
+    "kap_order", "osk_attention", "dense_attention", "mask_from_order", "order_from_mask",
+    "osk_attention_masked", "mask_words_for", "block_mass",
     "COSA_F32", "COSA_BF16", "EXPORTED_SYMBOLS",
 ]
 
@@ -36,7 +41,8 @@ _LIB = None
 EXPORTED_SYMBOLS = (
     "cosa_validate", "cosa_dims", "cosa_kap_workspace_size", "cosa_kap_order",
     "cosa_osk_attention", "cosa_dense_attention", "cosa_status_string",
-    "cosa_last_error", "cosa_version",
+    "cosa_last_error", "cosa_version", "cosa_mask_from_order", "cosa_order_from_mask",
+    "cosa_osk_attention_masked", "cosa_block_mass",
 )
 
 
@@ -88,6 +94,10 @@ def load():
         "cosa_kap_order": (i32, [P, vp, vp, i32, f64, vp, vp, vp, i32, vp, vp, vp, sz, vp]),
         "cosa_osk_attention": (i32, [P, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp, vp, vp, vp, vp]),
         "cosa_dense_attention": (i32, [P, vp, vp, vp, vp, vp, vp]),
+        "cosa_mask_from_order": (i32, [P, vp, vp, i32, vp, i32, vp]),
+        "cosa_order_from_mask": (i32, [P, vp, i32, vp, vp, i32, vp]),
+        "cosa_osk_attention_masked": (i32, [P, vp, vp, vp, vp, i32, i32, f32, vp, vp, vp, vp, vp]),
+        "cosa_block_mass": (i32, [P, vp, vp, vp, vp, vp]),
         "cosa_status_string": (ctypes.c_char_p, [i32]),
         "cosa_last_error": (ctypes.c_char_p, []),
         "cosa_version": (i32, []),
@@ -150,6 +160,27 @@ def cosa_osk_attention(problem, q, k_pages, v_pages, order, count, kmax, group,
 
 def cosa_dense_attention(problem, q, k_pages, v_pages, o, lse, stream) -> None:
     _check(load().cosa_dense_attention(ctypes.byref(problem), q, k_pages, v_pages, o, lse, stream))
+
+
+def cosa_mask_from_order(problem, order, count, kmax, mask, mask_words, stream) -> None:
+    _check(load().cosa_mask_from_order(ctypes.byref(problem), order, count, int(kmax), mask,
+                                       int(mask_words), stream))
+
+
+def cosa_order_from_mask(problem, mask, mask_words, order, count, kmax, stream) -> None:
+    _check(load().cosa_order_from_mask(ctypes.byref(problem), mask, int(mask_words), order, count,
+                                       int(kmax), stream))
+
+
+def cosa_osk_attention_masked(problem, q, k_pages, v_pages, mask, mask_words, group,
+                              skip_threshold, o, visited, skipped, lse, stream) -> None:
+    _check(load().cosa_osk_attention_masked(ctypes.byref(problem), q, k_pages, v_pages, mask,
+                                            int(mask_words), int(group), float(skip_threshold), o,
+                                            visited, skipped, lse, stream))
+
+
+def cosa_block_mass(problem, q, k_pages, lse, mass, stream) -> None:
+    _check(load().cosa_block_mass(ctypes.byref(problem), q, k_pages, lse, mass, stream))
 
 
 # ---- torch-facing helpers ---------------------------------------------------
@@ -275,6 +306,66 @@ def dense_attention(problem: Problem, q, k_pages, v_pages, *, lse: bool = False,
     if ls is not None:
         res["lse"] = ls
     return res
+
+
+def mask_words_for(problem: Problem) -> int:
+    return max(1, (problem.dims().max_nk + 63) // 64)
+
+
+def mask_from_order(problem: Problem, order, count, *, mask_words=None, stream=None):
+    """Binary block mask (int64 view of the uint64 words) of the listed blocks."""
+    import torch
+    d = problem.dims()
+    mw = mask_words_for(problem) if mask_words is None else int(mask_words)
+    mask = torch.empty((problem.c.batch, problem.c.h_kv, d.max_nq, mw), dtype=torch.int64, device=order.device)
+    cosa_mask_from_order(problem.c, order.data_ptr(), count.data_ptr(), int(order.shape[3]),
+                         mask.data_ptr(), mw, _stream(stream))
+    return mask
+
+
+def order_from_mask(problem: Problem, mask, kmax: int, *, device=None, stream=None):
+    """Ascending list of the selected causal blocks (mask None: every causal block);
+    returns dict(order, count)."""
+    import torch
+    d = problem.dims()
+    dev = mask.device if mask is not None else device
+    order = torch.empty((problem.c.batch, problem.c.h_kv, d.max_nq, int(kmax)), dtype=torch.int32, device=dev)
+    count = torch.empty(order.shape[:3], dtype=torch.int32, device=dev)
+    mw = int(mask.shape[3]) if mask is not None else 0
+    cosa_order_from_mask(problem.c, _ptr(mask), mw, order.data_ptr(), count.data_ptr(), int(kmax),
+                         _stream(stream))
+    return {"order": order, "count": count}
+
+
+def osk_attention_masked(problem: Problem, q, k_pages, v_pages, mask, tau: float, *, lse: bool = False,
+                         out=None, stream=None):
+    """Control-flow-skipping walk over a binary block mask; returns dict(O, visited, skipped[, lse])."""
+    import torch
+    dev = q.device
+    d = problem.dims()
+    o = torch.empty_like(q) if out is None else out
+    vis = torch.empty((problem.c.batch, problem.c.h_q, d.max_nq), dtype=torch.int32, device=dev)
+    skp = torch.empty_like(vis)
+    ls = torch.empty((problem.c.h_q, d.total_q), dtype=torch.float32, device=dev) if lse else None
+    cosa_osk_attention_masked(problem.c, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                              mask.data_ptr(), int(mask.shape[3]), problem.group, tau, o.data_ptr(),
+                              vis.data_ptr(), skp.data_ptr(), _ptr(ls), _stream(stream))
+    res = {"O": o, "visited": vis, "skipped": skp}
+    if ls is not None:
+        res["lse"] = ls
+    return res
+
+
+def block_mass(problem: Problem, q, k_pages, lse, *, stream=None):
+    """Exact attention mass [batch, h_q, max_nq, max_nk] of every causal block,
+    given the rows' log-sum-exp from ``dense_attention(..., lse=True)``."""
+    import torch
+    d = problem.dims()
+    mass = torch.empty((problem.c.batch, problem.c.h_q, d.max_nq, d.max_nk), dtype=torch.float32,
+                       device=q.device)
+    cosa_block_mass(problem.c, q.data_ptr(), k_pages.data_ptr(), lse.data_ptr(), mass.data_ptr(),
+                    _stream(stream))
+    return mass
 
 
 def dense_causal_flops(seqlens_q: Sequence[int], seqlens_k: Sequence[int], h_q: int, head_dim: int) -> float:

@@ -1,0 +1,212 @@
+"""Comparison modes of the CoSA path on one GPU (ablation and diagnostics).
+
+The CoSA summary credits its speed and accuracy to three parts acting
+together (§4, ablation): ordered selection by the proxy, in-kernel skipping,
+and page remapping (§2.3: unselected pages are jumped over instead of being
+branched around inside the kernel). This runner separates them on a seeded
+synthetic workload, all through the library's C ABI:
+
+    cosa        proxy list in HRM-first order, in-kernel skip (the method)
+    kap-only    proxy list, skipping off
+    ascending   proxy selection walked in ascending block order, skip on
+                (the order's effect on skipping)
+    mask-scan   proxy selection as a binary mask, control-flow walk over every
+                causal block, skip on (the remapping's effect; same blocks and
+                order as "ascending")
+    skip-only   every causal block in ascending order, skip on (a fixed-order
+                kernel with in-kernel skipping and no proxy)
+    dense       dense causal attention (the reference every mode is scored
+                against)
+
+Per mode: walk time (HIP events, median over the repetitions), proxy time,
+visited / skipped / computed (query head, query block, KV block) triples,
+computed share of the causal triples, and the output's error against dense
+attention. With --mass the exact block masses (the COBS page's oracle
+selector) score the proxy's selection: mean recall of the listed blocks
+against the best selection of the same size.
+
+    python -m block_sparse_attention_26_amd.ablation [--workload cfg2] [--budget B]
+        [--tau T] [--sink-logit X] [--reps R] [--mass] [--json PATH]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+WORKLOADS = {"cfg1": 1, "cfg2": 2, "cfg3": 3, "cfg4": 4, "cfg5": 5}
+MODES = ("cosa", "kap-only", "ascending", "mask-scan", "skip-only", "dense")
+
+
+def _log(*a):
+    print("[ablation]", *a, file=sys.stderr, flush=True)
+
+
+def _timed(fn, reps, stream):
+    import torch
+    out = None
+    times = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        out = fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    return out, statistics.median(times), min(times)
+
+
+def causal_triples(case) -> int:
+    """(query head, query block, KV block) triples a dense walk visits."""
+    B = case.block
+    total = 0
+    for lq, lk in zip(case.seqlens_q, case.seqlens_k.tolist()):
+        off = lk - lq
+        for qb in range(-(-lq // B)):
+            total += (off + min(qb * B + B - 1, lq - 1)) // B + 1
+    return total * case.h_q
+
+
+def run(args) -> list:
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_26_amd as cosa
+    sys.path.insert(0, ROOT)
+    import synthetic
+
+    if not torch.cuda.is_available():
+        raise SystemExit("the comparison modes run on a GPU")
+    kw = {}
+    if args.sink_logit is not None:
+        kw["sink_logit"] = args.sink_logit
+    case = synthetic.config_case(WORKLOADS[args.workload], budget=args.budget, **kw)
+    if args.tau is not None:
+        case.tau = args.tau
+    if case.dtype != "bf16":
+        raise SystemExit("the mask walk and block mass are built for bf16 workloads")
+    _log(f"{args.workload}: q {tuple(case.q.shape)}, budget {case.budget}, tau {case.tau:.3g}")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    q, k, v = case.q.to(dev), case.k_pages.to(dev), case.v_pages.to(dev)
+    pr = cosa.Problem.from_case(case, device=dev)
+    d = pr.dims(case.pool, case.budget)
+    tau = case.tau
+    reps = args.reps
+    causal = causal_triples(case)
+
+    # reference output and the proxy's lists
+    dn, dense_ms, dense_min = _timed(lambda: cosa.dense_attention(pr, q, k, v, lse=args.mass), reps, stream)
+    O_ref = dn["O"].float()
+    ref_norm = float(O_ref.norm())
+    ka, kap_ms, _ = _timed(lambda: cosa.kap_order(pr, q, k, case.pool, case.budget), reps, stream)
+    order, count = ka["order"], ka["count"]
+    mask, mask_ms, _ = _timed(lambda: cosa.mask_from_order(pr, order, count), reps, stream)
+    asc, asc_ms, _ = _timed(lambda: cosa.order_from_mask(pr, mask, d.kmax), reps, stream)
+    full, full_ms, _ = _timed(lambda: cosa.order_from_mask(pr, None, d.max_nk, device=dev), reps, stream)
+
+    walks = {
+        "cosa": (lambda: cosa.osk_attention(pr, q, k, v, order, count, tau), kap_ms),
+        "kap-only": (lambda: cosa.osk_attention(pr, q, k, v, order, count, 0.0), kap_ms),
+        "ascending": (lambda: cosa.osk_attention(pr, q, k, v, asc["order"], asc["count"], tau),
+                      kap_ms + mask_ms + asc_ms),
+        "mask-scan": (lambda: cosa.osk_attention_masked(pr, q, k, v, mask, tau), kap_ms + mask_ms),
+        "skip-only": (lambda: cosa.osk_attention(pr, q, k, v, full["order"], full["count"], tau), 0.0),
+    }
+    rows = []
+    for mode in MODES:
+        if mode == "dense":
+            res, ms, mn, proxy = dn, dense_ms, dense_min, 0.0
+            visited, skipped = causal, 0
+        else:
+            fn, proxy = walks[mode]
+            fn()  # warm
+            res, ms, mn = _timed(fn, reps, stream)
+            visited = int(res["visited"].sum())
+            skipped = int(res["skipped"].sum())
+        err = (res["O"].float() - O_ref)
+        row = {
+            "mode": mode,
+            "walk_ms": ms,
+            "walk_ms_min": mn,
+            "proxy_ms": proxy,
+            "total_ms": ms + proxy,
+            "visited": visited,
+            "skipped": skipped,
+            "computed": visited - skipped,
+            "skip_rate": skipped / visited if visited else 0.0,
+            "computed_share": (visited - skipped) / causal,
+            "rel_l2_vs_dense": float(err.norm()) / ref_norm if ref_norm > 0 else 0.0,
+            "max_abs_vs_dense": float(err.abs().max()),
+        }
+        rows.append(row)
+        _log(f"{mode:10s} walk {ms:8.3f} ms  proxy {proxy:6.3f} ms  computed {row['computed_share']:.4f}"
+             f"  skip rate {row['skip_rate']:.4f}  rel L2 {row['rel_l2_vs_dense']:.3e}")
+
+    if args.mass:
+        t0 = time.perf_counter()
+        M = cosa.block_mass(pr, q, k, dn["lse"])
+        torch.cuda.synchronize()
+        G = case.h_q // case.h_kv
+        Mg = M.view(case.batch, case.h_kv, G, d.max_nq, d.max_nk).sum(dim=2).double().cpu().numpy()
+        o = order.cpu().numpy().astype(np.int64)
+        c = count.cpu().numpy()
+        t = np.arange(o.shape[-1])
+        valid = t[None, None, None, :] < c[..., None]
+        picked = np.take_along_axis(Mg, np.where(valid, o, 0), axis=-1) * valid
+        tot = Mg.sum(axis=-1)
+        srt = -np.sort(-Mg, axis=-1)
+        top = np.where(np.arange(Mg.shape[-1])[None, None, None, :] < c[..., None], srt, 0.0).sum(axis=-1)
+        live = (c > 0) & (tot > 0)
+        rec = picked.sum(axis=-1)[live] / tot[live]
+        best = top[live] / tot[live]
+        summary = {
+            "mode": "mass-recall",
+            "kap_recall_mean": float(rec.mean()),
+            "kap_recall_min": float(rec.min()),
+            "oracle_recall_mean": float(best.mean()),
+            "oracle_recall_min": float(best.min()),
+            "rows": int(live.sum()),
+            "seconds": time.perf_counter() - t0,
+        }
+        rows.append(summary)
+        _log(f"mass recall: proxy {summary['kap_recall_mean']:.4f} (min {summary['kap_recall_min']:.4f}),"
+             f" oracle top-k {summary['oracle_recall_mean']:.4f} (min {summary['oracle_recall_min']:.4f})")
+
+    meta = {"workload": args.workload, "seq_len": case.seqlens_q if case.batch > 1 else case.seqlens_q[0],
+            "h_q": case.h_q, "h_kv": case.h_kv, "head_dim": case.head_dim, "block": case.block,
+            "pool": case.pool, "budget": case.budget, "skip_threshold": tau, "reps": reps,
+            "sink_logit": args.sink_logit, "causal_triples": causal}
+    for r in rows:
+        r["config"] = meta
+    return rows
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--workload", default="cfg2", choices=sorted(WORKLOADS))
+    ap.add_argument("--budget", type=float, default=None)
+    ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--sink-logit", type=float, default=None)
+    ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--mass", action="store_true")
+    ap.add_argument("--json", default=None, help="also append the JSON lines to this file")
+    args = ap.parse_args(argv)
+    rows = run(args)
+    for r in rows:
+        line = json.dumps(r)
+        print(line, flush=True)
+        if args.json:
+            with open(args.json, "a") as f:
+                f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -136,17 +136,43 @@ cosa_status hip_result(hipError_t e, const char* what) {
   return ok();
 }
 
+int32_t min_mask_words(const cosa_problem* p) {
+  cosa_dims_t d;
+  compute_dims(p, 0, 0.0, &d);
+  return (int32_t)cdiv(d.max_nk, 64);
+}
+
+cosa_status check_mask_words(const cosa_problem* p, int32_t mask_words, bool capped) {
+  const int32_t need = min_mask_words(p);
+  if (mask_words < std::max(need, 1))
+    return fail(COSA_ERR_INVALID_ARG, "mask_words (%d) must be >= ceil(max_nk / 64) = %d", mask_words,
+                std::max(need, 1));
+  if (capped && mask_words > 64)
+    return fail(COSA_ERR_UNSUPPORTED, "mask_words (%d) exceeds 64 (4096 KV blocks)", mask_words);
+  return COSA_OK;
+}
+
+// list walk (order/count), mask walk (mask) or dense walk
 cosa_status run_attention(const cosa_problem* p, const void* q, const void* k, const void* v,
-                          const int32_t* order, const int32_t* count, int32_t kmax, int32_t group,
+                          const int32_t* order, const int32_t* count, int32_t kmax,
+                          const uint64_t* mask, int32_t mask_words, int32_t group,
                           float tau, void* o, int32_t* visited, int32_t* skipped,
                           uint8_t* skip_bits, float* lse, void* stream, bool dense) {
   cosa_status st = validate(p);
   if (st != COSA_OK) return st;
   if (!q || !k || !v || !o) return fail(COSA_ERR_INVALID_ARG, "q, k_pages, v_pages and o must be non-NULL");
+  const bool masked = !dense && mask_words > 0;
+  if (masked) {
+    if (!mask || !visited || !skipped)
+      return fail(COSA_ERR_INVALID_ARG, "mask, visited and skipped must be non-NULL");
+    if ((st = check_mask_words(p, mask_words, false)) != COSA_OK) return st;
+    if (p->dtype != COSA_BF16)
+      return fail(COSA_ERR_UNSUPPORTED, "the mask walk is built for bf16 only");
+  }
   if (!dense) {
-    if (!order || !count || !visited || !skipped)
+    if (!masked && (!order || !count || !visited || !skipped))
       return fail(COSA_ERR_INVALID_ARG, "order, count, visited and skipped must be non-NULL");
-    if (kmax < 1) return fail(COSA_ERR_INVALID_ARG, "kmax must be >= 1 (got %d)", kmax);
+    if (!masked && kmax < 1) return fail(COSA_ERR_INVALID_ARG, "kmax must be >= 1 (got %d)", kmax);
     if (group != p->h_q / p->h_kv)
       return fail(COSA_ERR_INVALID_ARG, "group (%d) must equal h_q / h_kv (%d)", group, p->h_q / p->h_kv);
     if (!(tau >= 0.f && tau < 1.f))
@@ -167,6 +193,8 @@ cosa_status run_attention(const cosa_problem* p, const void* q, const void* k, c
   a.skipped = skipped;
   a.skip_bits = skip_bits;
   a.lse = lse;
+  a.mask = masked ? mask : nullptr;
+  a.mask_words = masked ? mask_words : 0;
   a.total_q = d.total_q;
   a.kmax = kmax;
   a.scale = p->softmax_scale;
@@ -175,7 +203,40 @@ cosa_status run_attention(const cosa_problem* p, const void* q, const void* k, c
   a.skip_thr_raw = a.skip_on ? (float)(log((double)tau) / (double)p->softmax_scale) : 0.f;
   a.n_units = (int64_t)p->batch * p->h_q * d.max_nq;
   return hip_result(cosa::launch_osk(a, p->dtype, p->head_dim, p->block, dense, (hipStream_t)stream),
-                    dense ? "dense attention launch" : "OSK launch");
+                    dense ? "dense attention launch" : (masked ? "masked OSK launch" : "OSK launch"));
+}
+
+cosa_status run_mask_conversion(const cosa_problem* p, const int32_t* order, const int32_t* count,
+                                int32_t kmax, uint64_t* mask_out, const uint64_t* mask_in,
+                                int32_t mask_words, int32_t* order_out, int32_t* count_out,
+                                void* stream, bool to_mask) {
+  cosa_status st = validate(p);
+  if (st != COSA_OK) return st;
+  if (to_mask ? (!order || !count || !mask_out) : (!order_out || !count_out))
+    return fail(COSA_ERR_INVALID_ARG, to_mask ? "order, count and mask must be non-NULL"
+                                              : "order and count must be non-NULL");
+  if (kmax < 1) return fail(COSA_ERR_INVALID_ARG, "kmax must be >= 1 (got %d)", kmax);
+  if ((to_mask || mask_in) && (st = check_mask_words(p, mask_words, true)) != COSA_OK) return st;
+  if (!to_mask && !mask_in && min_mask_words(p) > 64)
+    return fail(COSA_ERR_UNSUPPORTED, "more than 4096 KV blocks per sequence");
+  cosa_dims_t d;
+  compute_dims(p, 0, 0.0, &d);
+  cosa::MaskArgs a{};
+  a.seq = seq_args(p, d);
+  a.block = p->block;
+  a.n_rows = (int64_t)p->batch * p->h_kv * d.max_nq;
+  if (a.n_rows == 0) return ok();
+  a.mask_words = mask_words;
+  a.kmax = kmax;
+  a.order = order;
+  a.count = count;
+  a.mask_out = mask_out;
+  a.mask_in = mask_in;
+  a.order_out = order_out;
+  a.count_out = count_out;
+  return hip_result(to_mask ? cosa::launch_mask_from_order(a, (hipStream_t)stream)
+                            : cosa::launch_order_from_mask(a, (hipStream_t)stream),
+                    to_mask ? "mask-from-order launch" : "order-from-mask launch");
 }
 
 }  // namespace
@@ -269,13 +330,57 @@ cosa_status cosa_osk_attention(const cosa_problem* problem, const void* q, const
                                int32_t kmax, int32_t group, float skip_threshold, void* o,
                                int32_t* visited, int32_t* skipped, uint8_t* skip_bits, float* lse,
                                void* stream) {
-  return run_attention(problem, q, k_pages, v_pages, order, count, kmax, group, skip_threshold, o,
-                       visited, skipped, skip_bits, lse, stream, false);
+  return run_attention(problem, q, k_pages, v_pages, order, count, kmax, nullptr, 0, group,
+                       skip_threshold, o, visited, skipped, skip_bits, lse, stream, false);
+}
+
+cosa_status cosa_osk_attention_masked(const cosa_problem* problem, const void* q, const void* k_pages,
+                                      const void* v_pages, const uint64_t* mask, int32_t mask_words,
+                                      int32_t group, float skip_threshold, void* o, int32_t* visited,
+                                      int32_t* skipped, float* lse, void* stream) {
+  if (mask_words < 1) return fail(COSA_ERR_INVALID_ARG, "mask_words must be >= 1 (got %d)", mask_words);
+  return run_attention(problem, q, k_pages, v_pages, nullptr, nullptr, 0, mask, mask_words, group,
+                       skip_threshold, o, visited, skipped, nullptr, lse, stream, false);
+}
+
+cosa_status cosa_mask_from_order(const cosa_problem* problem, const int32_t* order, const int32_t* count,
+                                 int32_t kmax, uint64_t* mask, int32_t mask_words, void* stream) {
+  return run_mask_conversion(problem, order, count, kmax, mask, nullptr, mask_words, nullptr, nullptr,
+                             stream, true);
+}
+
+cosa_status cosa_block_mass(const cosa_problem* problem, const void* q, const void* k_pages,
+                            const float* lse, float* mass, void* stream) {
+  cosa_status st = validate(problem);
+  if (st != COSA_OK) return st;
+  if (!q || !k_pages || !lse || !mass)
+    return fail(COSA_ERR_INVALID_ARG, "q, k_pages, lse and mass must be non-NULL");
+  if (problem->dtype != COSA_BF16) return fail(COSA_ERR_UNSUPPORTED, "block mass is built for bf16 only");
+  cosa_dims_t d;
+  compute_dims(problem, 0, 0.0, &d);
+  cosa::MassArgs a{};
+  a.seq = seq_args(problem, d);
+  a.q = q;
+  a.k = k_pages;
+  a.lse = lse;
+  a.mass = mass;
+  a.total_q = d.total_q;
+  a.scale_log2 = (float)((double)problem->softmax_scale * 1.4426950408889634);
+  a.n_units = (int64_t)problem->batch * problem->h_q * d.max_nq;
+  if (a.n_units == 0 || d.max_nk == 0) return ok();
+  return hip_result(cosa::launch_block_mass(a, problem->head_dim, problem->block, (hipStream_t)stream),
+                    "block-mass launch");
+}
+
+cosa_status cosa_order_from_mask(const cosa_problem* problem, const uint64_t* mask, int32_t mask_words,
+                                 int32_t* order, int32_t* count, int32_t kmax, void* stream) {
+  return run_mask_conversion(problem, nullptr, nullptr, kmax, nullptr, mask, mask_words, order, count,
+                             stream, false);
 }
 
 cosa_status cosa_dense_attention(const cosa_problem* problem, const void* q, const void* k_pages,
                                  const void* v_pages, void* o, float* lse, void* stream) {
-  return run_attention(problem, q, k_pages, v_pages, nullptr, nullptr, 1,
+  return run_attention(problem, q, k_pages, v_pages, nullptr, nullptr, 1, nullptr, 0,
                        problem ? problem->h_q / std::max(problem->h_kv, 1) : 1, 0.f, o, nullptr,
                        nullptr, nullptr, lse, stream, true);
 }

@@ -14,10 +14,6 @@ constexpr int kNumXcd = 8;
 // Largest KV-block count per sequence the proxy's in-LDS sort handles.
 constexpr int kMaxSortBlocks = 4096;
 
-// Longest list the two-head attention kernel stages in LDS (longer lists, or
-// a dense walk over more blocks, take the single-head kernel).
-constexpr int kMaxDbList = 4096;
-
 struct SeqArgs {
   const int32_t* cu_seqlens_q;  // [batch+1]
   const int32_t* seqlens_k;     // [batch]
@@ -39,6 +35,8 @@ struct OskArgs {
   int32_t* skipped;      // [batch, h_q, max_nq]       (null for dense)
   uint8_t* skip_bits;    // [batch, h_q, max_nq, kmax] (nullable)
   float* lse;            // [h_q, total_q]             (nullable)
+  const uint64_t* mask;  // [batch, h_kv, max_nq, mask_words] binary block mask (mask walk only)
+  int32_t mask_words;
   int32_t total_q;
   int32_t kmax;
   float scale;           // softmax scale
@@ -69,10 +67,40 @@ struct KapArgs {
   float scale;
 };
 
+// Mask <-> list conversions (one wave per row of batch * h_kv * max_nq).
+struct MaskArgs {
+  SeqArgs seq;
+  int32_t block;
+  int64_t n_rows;
+  int32_t mask_words;        // <= 64
+  int32_t kmax;
+  const int32_t* order;      // list -> mask input
+  const int32_t* count;
+  uint64_t* mask_out;
+  const uint64_t* mask_in;   // mask -> list input (null: every causal block)
+  int32_t* order_out;
+  int32_t* count_out;
+};
+
+// Exact block attention mass (one workgroup per batch * h_q * max_nq unit).
+struct MassArgs {
+  SeqArgs seq;
+  const void* q;
+  const void* k;
+  const float* lse;   // [h_q, total_q] natural-log sum-exp per row
+  float* mass;        // [batch, h_q, max_nq, max_nk]
+  int32_t total_q;
+  float scale_log2;
+  int64_t n_units;
+};
+
 // Each launcher returns hipSuccess or the launch error. `dtype` is cosa_dtype.
 hipError_t launch_osk(const OskArgs& a, int dtype, int head_dim, int block, bool dense,
                       hipStream_t stream);
 hipError_t launch_osk_bf16(const OskArgs& a, int head_dim, int block, bool dense, hipStream_t stream);
 hipError_t launch_kap(const KapArgs& a, int dtype, int head_dim, int block, hipStream_t stream);
+hipError_t launch_mask_from_order(const MaskArgs& a, hipStream_t stream);
+hipError_t launch_order_from_mask(const MaskArgs& a, hipStream_t stream);
+hipError_t launch_block_mass(const MassArgs& a, int head_dim, int block, hipStream_t stream);
 
 }  // namespace cosa

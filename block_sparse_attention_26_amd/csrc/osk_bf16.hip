@@ -98,8 +98,15 @@ struct Geo {
   __device__ static constexpr int swz_v(int r) { return D == 128 ? 4 * (r % 4) : 4 * (r % 2); }
 };
 
-template <int D, int BLK, bool DENSE>
+// Walk modes: the ordered list (the OSK), every causal block ascending (the
+// dense baseline), or every causal block ascending under a binary block mask
+// (control-flow skipping, for comparison with the list walk).
+enum WalkMode { kList = 0, kDense = 1, kMask = 2 };
+
+template <int D, int BLK, int MODE>
 __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
+  constexpr bool DENSE = MODE == kDense;
+  constexpr bool MASK = MODE == kMask;
   using Gm = Geo<D, BLK>;
   constexpr int NW = Gm::NW, KT = Gm::KT, DT = Gm::DT, QREGS = Gm::QREGS;
   constexpr int CH = Gm::CH, ROWB = Gm::ROWB, TILE = Gm::TILE, NL = Gm::NL, RPC = Gm::RPC;
@@ -133,7 +140,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
         a.visited[out_row] = 0;
         a.skipped[out_row] = 0;
       }
-      if (a.skip_bits)
+      if (!MASK && a.skip_bits)
         for (int t = tid; t < a.kmax; t += Gm::THREADS) a.skip_bits[out_row * a.kmax + t] = 255;
     }
     return;
@@ -162,10 +169,12 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
 
   int n_list;
   const int32_t* lst = nullptr;
-  if constexpr (DENSE) {
+  const uint64_t* mrow = nullptr;
+  const int64_t list_row = ((int64_t)b * sq.h_kv + g) * sq.max_nq + qb;
+  if constexpr (DENSE || MASK) {
     n_list = n_causal;
+    if constexpr (MASK) mrow = a.mask + list_row * a.mask_words;
   } else {
-    const int64_t list_row = ((int64_t)b * sq.h_kv + g) * sq.max_nq + qb;
     n_list = min(__builtin_amdgcn_readfirstlane(a.count[list_row]), a.kmax);  // a corrupt count cannot overrun the row
     lst = a.order + list_row * a.kmax;
   }
@@ -194,7 +203,13 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
   // for entry t+1 are issued a tile ahead (after barrier A of tile t) and read
   // after barrier C, so their latency hides under the tile's work. An entry
   // that is not a causal block of the row, or a page out of range, sets `bad`.
-  auto entry_at = [&](int t) -> int { return DENSE ? t : lst[t]; };
+  auto entry_at = [&](int t) -> int { return MODE == kList ? lst[t] : t; };
+  // mask word of block i (uniform; i < n_causal <= 64 * mask_words)
+  auto mask_word = [&](int i) -> uint64_t {
+    const uint64_t x = mrow[i >> 6];
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32) |
+           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  };
   auto check_kb = [&](int raw) -> int {
     int kb = __builtin_amdgcn_readfirstlane(raw);  // uniform: keeps the mask branch scalar
     if (kb < 0 || kb >= n_causal) {
@@ -262,7 +277,13 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
   int kb = 0, page = 0;  // entry t
   int raw_e = 0;         // entry t+1, loaded a tile ahead
   Copy ck{}, cv{};
-  if (n_list > 0) {  // an empty list touches no entry
+  // mask walk: the block whose K copies are issued or pending (-1: none), the
+  // mask word of the current block, selected blocks walked
+  uint64_t mword = 0;
+  int n_vis = 0;
+  if (MASK) {
+    kb = -1;
+  } else if (n_list > 0) {  // an empty list touches no entry
     kb = check_kb(entry_at(0));
     page = check_page(table[kb]);
     ck = copy_of(page, true);
@@ -272,6 +293,24 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
   }
   bool pend = false;  // K(t) still to be issued: the previous block was skipped
   for (int t = 0; t < n_list; ++t) {
+    if constexpr (MASK) {
+      // control-flow skipping: every causal block costs a bit test; a block
+      // whose K was not prefetched (its predecessor unselected) is fetched
+      // here, with its latency exposed
+      for (;;) {
+        if ((t & 63) == 0) mword = mask_word(t);
+        if ((mword >> (t & 63)) & 1) break;
+        if (++t == n_list) break;
+      }
+      if (t == n_list) break;
+      ++n_vis;
+      if (kb != t) {
+        kb = t;
+        page = check_page(table[t]);
+        ck = copy_of(page, true);
+        pend = true;
+      }
+    }
     if (pend) {
 #pragma unroll 1
       for (int n = 0; n < NL; ++n) issue(ck, true, n);
@@ -280,9 +319,22 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
     __syncthreads();  // A: K(t) landed; every wave is done with V(t-1)
     // entry t+1 (the last entry again after the end, which keeps the K copies
     // of the next step unconditional) and its page; entry t+2
-    const int kb_next = check_kb(raw_e);
-    const int raw_p = table[kb_next];
-    raw_e = entry_at(min(t + 2, n_list - 1));
+    int kb_next, raw_p;
+    bool nsel = true;  // block t+1 is walked, so its K is prefetched during this block's P.V
+    if constexpr (MASK) {
+      kb_next = min(t + 1, n_list - 1);
+      raw_p = table[kb_next];
+      if (t + 1 < n_list) {
+        const uint64_t wn = ((t + 1) & 63) ? mword : mask_word(t + 1);
+        nsel = ((wn >> ((t + 1) & 63)) & 1) != 0;
+      } else {
+        nsel = false;
+      }
+    } else {
+      kb_next = check_kb(raw_e);
+      raw_p = table[kb_next];
+      raw_e = entry_at(min(t + 2, n_list - 1));
+    }
     const int nvalid = min(BLK, Lk - kb * BLK);
     cv = copy_of(page, false);  // V(t): copies issued during the S k-steps
 
@@ -354,7 +406,9 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
     }
     // K(t+1): copies issued during P.V (drained before exit)
     const int page_next = check_page(raw_p);
-    ck = copy_of(page_next, true);
+    // (mask walk, next block unselected: the copies re-read this block's K
+    // page, an L2 hit, so the copy sequence stays branch-free)
+    ck = copy_of(nsel ? page_next : page, true);
     constexpr int KPS = (NL + 2 * KT - 1) / (2 * KT);  // K copies per P.V k-step
 
     // ---- online-softmax update and O^T += V^T P^T, one 32-key tile at a time:
@@ -433,11 +487,11 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
       }
       l_run = l_run * alpha + rs;
     }
-    pend = skip;
-    if constexpr (!DENSE) {
+    pend = skip && nsel;
+    if constexpr (MODE == kList) {
       if (tid == 0 && a.skip_bits) a.skip_bits[out_row * a.kmax + t] = skip ? 1 : 0;
     }
-    kb = kb_next;
+    kb = nsel ? kb_next : -1;
     page = page_next;
   }
 
@@ -468,10 +522,10 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
   }
   if constexpr (!DENSE) {
     if (tid == 0) {
-      a.visited[out_row] = n_list;
+      a.visited[out_row] = MASK ? n_vis : n_list;
       a.skipped[out_row] = n_skip;
     }
-    if (a.skip_bits)
+    if (!MASK && a.skip_bits)
       for (int t = n_list + tid; t < a.kmax; t += Gm::THREADS) a.skip_bits[out_row * a.kmax + t] = 255;
   }
 }
@@ -481,9 +535,11 @@ hipError_t launch_one(const OskArgs& a, bool dense, hipStream_t stream) {
   const int64_t per = (int64_t)kNumXcd * a.seq.group;
   const int64_t grid = (a.n_units + per - 1) / per * per;
   if (dense)
-    hipLaunchKernelGGL((osk_bf16_kernel<D, BLK, true>), dim3((unsigned)grid), dim3(2 * BLK), 0, stream, a);
+    hipLaunchKernelGGL((osk_bf16_kernel<D, BLK, kDense>), dim3((unsigned)grid), dim3(2 * BLK), 0, stream, a);
+  else if (a.mask)
+    hipLaunchKernelGGL((osk_bf16_kernel<D, BLK, kMask>), dim3((unsigned)grid), dim3(2 * BLK), 0, stream, a);
   else
-    hipLaunchKernelGGL((osk_bf16_kernel<D, BLK, false>), dim3((unsigned)grid), dim3(2 * BLK), 0, stream, a);
+    hipLaunchKernelGGL((osk_bf16_kernel<D, BLK, kList>), dim3((unsigned)grid), dim3(2 * BLK), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -193,6 +193,63 @@ cosa_status cosa_osk_attention(const cosa_problem* problem, const void* q, const
 cosa_status cosa_dense_attention(const cosa_problem* problem, const void* q, const void* k_pages,
                                  const void* v_pages, void* o, float* lse, void* stream);
 
+/* ---- Binary block masks (comparison modes) -----------------------------------
+ * The CoSA summary contrasts its computation-order list (§2.1) with the
+ * binary masks of earlier proxies, and its page-remapped walk (§2.3,
+ * "mask-skipped" blocks are jumped over) with the control-flow skipping of
+ * standard sparse kernels; its ablation (§4) separates ordered selection,
+ * in-kernel skipping and remapping. These calls run one selection either way.
+ *
+ * mask  uint64 [batch, h_kv, max_nq, mask_words]: bit (kb % 64) of word
+ *       kb / 64 selects KV block kb for (b, g, qb). mask_words >=
+ *       ceil(max_nk / 64). Bits of non-causal blocks (kb >= n(qb)) are
+ *       ignored by every reader and cleared by cosa_mask_from_order. */
+
+/* mask = the set of causal blocks listed in order[.., 0 .. count-1] (entries
+ * outside 0 .. n(qb)-1 are ignored; the visit order is dropped). Rows past a
+ * sequence's end are all zero. Limits: mask_words <= 64. */
+cosa_status cosa_mask_from_order(const cosa_problem* problem, const int32_t* order,
+                                 const int32_t* count, int32_t kmax, uint64_t* mask,
+                                 int32_t mask_words, void* stream);
+
+/* order = the selected causal blocks of each row in ascending kb, truncated to
+ * the first kmax; count = the number written; -1 pads the row. mask may be
+ * NULL: every causal block is selected (with kmax >= max_nk, the dense walk
+ * as a list, so in-kernel skipping can run without any proxy). Rows past a
+ * sequence's end get count 0. Limits: max_nk <= 4096 (mask_words <= 64). */
+cosa_status cosa_order_from_mask(const cosa_problem* problem, const uint64_t* mask,
+                                 int32_t mask_words, int32_t* order, int32_t* count, int32_t kmax,
+                                 void* stream);
+
+/* cosa_osk_attention over a binary mask instead of a list: each row walks all
+ * of its causal blocks in ascending order, tests the block's bit and branches
+ * over unselected blocks (control-flow skipping). A selected block is
+ * prefetched only while the previous block is selected too; after a gap its
+ * pages are fetched on arrival. Selected blocks get the same skip test and
+ * update as in cosa_osk_attention, so the output equals that of
+ * cosa_osk_attention on cosa_order_from_mask's ascending list, bit for bit.
+ * visited = selected causal blocks walked; skipped = blocks skipped in-kernel.
+ * bf16 only (COSA_ERR_UNSUPPORTED for fp32). */
+cosa_status cosa_osk_attention_masked(const cosa_problem* problem, const void* q,
+                                      const void* k_pages, const void* v_pages,
+                                      const uint64_t* mask, int32_t mask_words, int32_t group,
+                                      float skip_threshold, void* o, int32_t* visited,
+                                      int32_t* skipped, float* lse, void* stream);
+
+/* Exact attention mass of every causal block, the ranking of the oracle
+ * selector on the COBS page ("Oracle Sparse Attention": keep the blocks that
+ * hold the most exact softmax mass), against which a proxy's selection can be
+ * scored (a diagnostic; it costs the QK^T of dense attention).
+ *  lse   fp32 [h_q, total_q]: natural-log sum-exp of each row over its
+ *        visible keys, as cosa_dense_attention writes it.
+ *  mass  fp32 [batch, h_q, max_nq, max_nk]: sum over the valid rows of qb and
+ *        the visible keys of kb of exp(softmax_scale * q.k - lse); 0 for
+ *        non-causal blocks and rows past a sequence's end; NaN for a block
+ *        whose page is outside the pool. A query row's masses add up to 1.
+ * bf16 only (COSA_ERR_UNSUPPORTED for fp32). */
+cosa_status cosa_block_mass(const cosa_problem* problem, const void* q, const void* k_pages,
+                            const float* lse, float* mass, void* stream);
+
 /* Static description of a status code. */
 const char* cosa_status_string(cosa_status status);
 

@@ -31,7 +31,9 @@ Modules:
     kap    - the Kernel-Aware Proxy: pooling, proxy scores, MaxNorm, HRM,
              flag-grouped sort and budget truncation.
     osk    - ordered online-softmax accumulation with the in-kernel skip rule.
+    masks  - binary block masks <-> ascending lists, exact block attention
+             mass and the recall of a selection (comparison modes).
     layout - causal block arithmetic and page gathering used by the above.
     cases  - convenience wrappers that run the oracle on a whole packed batch.
 """
-from . import exp32, dense, kap, osk, layout, cases  # noqa: F401
+from . import exp32, dense, kap, osk, masks, layout, cases  # noqa: F401

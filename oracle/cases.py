@@ -18,8 +18,9 @@ import numpy as np
 
 from . import dense as _dense
 from . import kap as _kap
+from . import masks as _masks
 from . import osk as _osk
-from .layout import cdiv, gather_pages, kmax as _kmax
+from .layout import cdiv, gather_pages, kmax as _kmax, n_causal_blocks
 
 
 def _f64(t) -> np.ndarray:
@@ -136,3 +137,30 @@ def dense_case(case, rows_per_seq=None):
         O[cu[b] + idx] = o
         lse[:, cu[b] + idx] = ls
     return {"O": O, "lse": lse}
+
+
+def n_causal_rows(case) -> np.ndarray:
+    """Causal KV blocks of every row [batch, h_kv, max_nq] (0 past a sequence's end)."""
+    dm = dims(case)
+    B = case.block
+    n = np.zeros((case.batch, case.h_kv, dm["max_nq"]), dtype=np.int64)
+    for b in range(case.batch):
+        Lq, Lk = case.seqlens_q[b], int(case.seqlens_k[b])
+        for qb in range(cdiv(Lq, B)):
+            n[b, :, qb] = n_causal_blocks(qb, B, Lq, Lk)
+    return n
+
+
+def block_mass_case(case) -> np.ndarray:
+    """Exact block mass [batch, h_q, max_nq, max_nk] over the batch (fp64)."""
+    dm = dims(case)
+    M = np.zeros((case.batch, case.h_q, dm["max_nq"], dm["max_nk"]))
+    G = case.h_q // case.h_kv
+    for b in range(case.batch):
+        Lq, Lk = case.seqlens_q[b], int(case.seqlens_k[b])
+        if Lq == 0:
+            continue
+        q, k, _ = sequence_inputs(case, b)
+        M[b, :, : cdiv(Lq, case.block), : cdiv(Lk, case.block)] = _masks.block_mass_sequence(
+            q, k, case.scale, G, case.block)
+    return M

@@ -125,3 +125,55 @@ def test_workspace_size_and_argument_errors():
             cosa.cosa_osk_attention(p.c, ptr, ptr, ptr, ptr, ptr, args["kmax"], args["group"],
                                     args["tau"], ptr, ptr, ptr, None, None, None)
         assert e.value.status == -1
+
+
+def test_mask_entry_points_reject_bad_arguments():
+    _lib_or_skip()
+    p = _problem((131072,))  # 1024 KV blocks: 16 mask words
+    buf = FakeDev(1, 16)
+    ptr = buf.data_ptr()
+    for mw, status in [(15, -1), (0, -1), (65, -2)]:
+        with pytest.raises(cosa.CosaError) as e:
+            cosa.cosa_mask_from_order(p.c, ptr, ptr, 103, ptr, mw, None)
+        assert e.value.status == status, mw
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_mask_from_order(p.c, ptr, ptr, 0, ptr, 16, None)  # kmax
+    assert e.value.status == -1
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_mask_from_order(p.c, None, ptr, 103, ptr, 16, None)
+    assert e.value.status == -1
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_order_from_mask(p.c, ptr, 15, ptr, ptr, 103, None)
+    assert e.value.status == -1
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_order_from_mask(p.c, None, 0, None, ptr, 103, None)
+    assert e.value.status == -1
+    # more than 4096 KV blocks: no one-wave-per-row conversion
+    big = _problem((1024,), (4097 * 128,))
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_order_from_mask(big.c, None, 0, ptr, ptr, 4097, None)
+    assert e.value.status == -2
+    for bad in [dict(mw=15), dict(mw=0), dict(group=3), dict(tau=1.0)]:
+        args = dict(mw=16, group=4, tau=1e-7)
+        args.update(bad)
+        with pytest.raises(cosa.CosaError) as e:
+            cosa.cosa_osk_attention_masked(p.c, ptr, ptr, ptr, ptr, args["mw"], args["group"],
+                                           args["tau"], ptr, ptr, ptr, None, None)
+        assert e.value.status == -1, bad
+    f32 = _problem((1024,), h_q=1, h_kv=1, d=64, B=64, dtype=cosa.COSA_F32)
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_osk_attention_masked(f32.c, ptr, ptr, ptr, ptr, 1, 1, 0.0, ptr, ptr, ptr, None, None)
+    assert e.value.status == -2
+
+
+def test_block_mass_rejects_bad_arguments():
+    _lib_or_skip()
+    p = _problem((2048,))
+    ptr = FakeDev(1, 16).data_ptr()
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_block_mass(p.c, ptr, ptr, None, ptr, None)
+    assert e.value.status == -1
+    f32 = _problem((1024,), h_q=1, h_kv=1, d=64, B=64, dtype=cosa.COSA_F32)
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_block_mass(f32.c, ptr, ptr, ptr, ptr, None)
+    assert e.value.status == -2
