@@ -145,6 +145,10 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
   constexpr int ROWS = kScoreRows * RT;  // pooled query rows per workgroup
   // LDS reduction (blocks of 1, 2, 64 or 128 pooled keys), double-buffered
   __shared__ float tile[RT == 1 ? 2 : 1][RT == 1 ? kScoreRows : 1][kScoreKeys + 1];
+  // RT > 1: block maxima staged per chunk of CB blocks (double-buffered) so
+  // that P is written in whole 128-byte row segments
+  constexpr int CB = 32;
+  __shared__ float pst[RT > 1 ? 2 : 1][RT > 1 ? ROWS : 1][CB + 1];
   const SeqArgs& sq = a.seq;
   const int G = sq.group;
   const int ntile = (a.max_nr + ROWS - 1) / ROWS;
@@ -230,8 +234,11 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
 #pragma unroll
   for (int u = 0; u < RT; ++u) rmx[u] = kNegInf;
   int it = 0;
+  // the tile's first row sees the fewest keys
+  const int jmax_first = (off + min(r0 * p + p - 1, Lq - 1)) / p;
   for (int j0 = 0; j0 < jend; j0 += kScoreKeys, ++it) {
     const int64_t koff_n = j0 + kScoreKeys < jend ? key_off(j0 + kScoreKeys) : -1;
+    const bool edge = j0 + kScoreKeys - 1 > jmax_first || j0 + kScoreKeys > Rk;
     if constexpr (BF16) {
       const uint16_t* kp = (const uint16_t*)a.k_pool + (koff_n < 0 ? 0 : koff_n) + hl * 8;
 #pragma unroll
@@ -263,10 +270,27 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
     for (int u = 0; u < RT; ++u) {
       // element v of this lane: key jj = w*32 + 8*(v/4) + 4*hl + v%4 of the step
       float x[16];
+      if constexpr (RT > 1) {
+        // Raw dot products; the scale is applied after the max-pool (rounding
+        // of scale*x is monotone in x, so max then scale gives the same bits).
+        // Only steps that reach the first row's causal edge or the key range
+        // end need the mask.
+        if (edge) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int j = j0 + w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3);
-        x[v] = (j <= my_jmax[u] && j < Rk) ? sc[u][v] * a.scale : kNegInf;
+          for (int v = 0; v < 16; ++v) {
+            const int j = j0 + w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3);
+            x[v] = (j <= my_jmax[u] && j < Rk) ? sc[u][v] : kNegInf;
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) x[v] = sc[u][v];
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int j = j0 + w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3);
+          x[v] = (j <= my_jmax[u] && j < Rk) ? sc[u][v] * a.scale : kNegInf;
+        }
       }
       if constexpr (RT > 1) {
         // blocks of 4..32 keys lie inside one wave's 32 keys: maxima in
@@ -283,8 +307,8 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
         rmx[u] = fmaxf(rmx[u], fmaxf(fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1])),
                                      fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3]))));
         if (hl == 0 && r < R) {
-          float* prow = P + (int64_t)r * sq.max_nk;
           const int kbase = (j0 + w * 32) / per;
+          float* srow = pst[(kbase / CB) & 1][u * kScoreRows + l32] + kbase % CB;
           float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
           int nb;
           if (per == 4) {  // block 2q + half
@@ -309,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
           }
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            if (i < nb && kbase + i < kb_end) prow[kbase + i] = m[i];
+            if (i < nb) srow[i] = m[i];
         }
       } else {
         float (*tl)[kScoreKeys + 1] = tile[it & 1];
@@ -329,6 +353,19 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
         }
       }
     }
+    if constexpr (RT > 1) {
+      // last step of a chunk of CB blocks: write the chunk's rows, scaled
+      const int cks = CB * per;  // keys per chunk
+      if ((j0 + kScoreKeys) % cks == 0 || j0 + kScoreKeys >= jend) {
+        const int ch = j0 / cks;
+        __syncthreads();
+        for (int i = tid; i < ROWS * CB; i += kThreads) {
+          const int rr = i / CB, c = i % CB;
+          const int r = r0 + rr, kb = ch * CB + c;
+          if (r < R && kb < kb_end) P[(int64_t)r * sq.max_nk + kb] = pst[ch & 1][rr][c] * a.scale;
+        }
+      }
+    }
     if constexpr (BF16) {
 #pragma unroll
       for (int ks = 0; ks < QREGS; ++ks) kc[ks] = kn[ks];
@@ -344,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
       __shared__ float part[kThreads / 64][ROWS];
       if (hl == 0)
 #pragma unroll
-        for (int u = 0; u < RT; ++u) part[w][u * kScoreRows + l32] = rmx[u];
+        for (int u = 0; u < RT; ++u) part[w][u * kScoreRows + l32] = rmx[u] * a.scale;
       __syncthreads();
       for (int i = tid; i < ROWS; i += kThreads) {
         const int r = r0 + i;
