@@ -8,11 +8,12 @@ point raises.
 Low-level functions carry the C names (``cosa_kap_order``,
 ``cosa_osk_attention``, ``cosa_dense_attention``, ``cosa_mask_from_order``,
 ``cosa_order_from_mask``, ``cosa_osk_attention_masked``, ``cosa_block_mass``,
+``cosa_union_order``,
 ``cosa_validate``,
 ``cosa_dims``, ``cosa_kap_workspace_size``) and take integer device pointers.
 The ``Problem`` class and the ``kap_order`` / ``osk_attention`` /
 ``dense_attention`` / ``mask_from_order`` / ``order_from_mask`` /
-``osk_attention_masked`` / ``block_mass`` helpers accept torch tensors that already live on the
+``osk_attention_masked`` / ``block_mass`` / ``union_order`` helpers accept torch tensors that already live on the
 GPU and allocate the outputs with torch.
 """
 from __future__ import annotations
@@ -27,9 +28,9 @@ __all__ = [
     "cosa_validate", "cosa_dims", "cosa_kap_workspace_size", "cosa_kap_order",
     "cosa_osk_attention", "cosa_dense_attention", "cosa_status_string",
     "cosa_last_error", "cosa_version", "cosa_mask_from_order", "cosa_order_from_mask",
-    "cosa_osk_attention_masked", "cosa_block_mass",
+    "cosa_osk_attention_masked", "cosa_block_mass", "cosa_union_order",
     "kap_order", "osk_attention", "dense_attention", "mask_from_order", "order_from_mask",
-    "osk_attention_masked", "mask_words_for", "block_mass",
+    "osk_attention_masked", "mask_words_for", "block_mass", "union_order",
     "COSA_F32", "COSA_BF16", "EXPORTED_SYMBOLS",
 ]
 
@@ -42,7 +43,7 @@ EXPORTED_SYMBOLS = (
     "cosa_validate", "cosa_dims", "cosa_kap_workspace_size", "cosa_kap_order",
     "cosa_osk_attention", "cosa_dense_attention", "cosa_status_string",
     "cosa_last_error", "cosa_version", "cosa_mask_from_order", "cosa_order_from_mask",
-    "cosa_osk_attention_masked", "cosa_block_mass",
+    "cosa_osk_attention_masked", "cosa_block_mass", "cosa_union_order",
 )
 
 
@@ -98,6 +99,7 @@ def load():
         "cosa_order_from_mask": (i32, [P, vp, i32, vp, vp, i32, vp]),
         "cosa_osk_attention_masked": (i32, [P, vp, vp, vp, vp, i32, i32, f32, vp, vp, vp, vp, vp]),
         "cosa_block_mass": (i32, [P, vp, vp, vp, vp, vp]),
+        "cosa_union_order": (i32, [P, vp, vp, i32, vp, vp, i32, vp]),
         "cosa_status_string": (ctypes.c_char_p, [i32]),
         "cosa_last_error": (ctypes.c_char_p, []),
         "cosa_version": (i32, []),
@@ -177,6 +179,11 @@ def cosa_osk_attention_masked(problem, q, k_pages, v_pages, mask, mask_words, gr
     _check(load().cosa_osk_attention_masked(ctypes.byref(problem), q, k_pages, v_pages, mask,
                                             int(mask_words), int(group), float(skip_threshold), o,
                                             visited, skipped, lse, stream))
+
+
+def cosa_union_order(problem, order, count, kmax, union_order, union_count, union_kmax, stream) -> None:
+    _check(load().cosa_union_order(ctypes.byref(problem), order, count, int(kmax), union_order,
+                                   union_count, int(union_kmax), stream))
 
 
 def cosa_block_mass(problem, q, k_pages, lse, mass, stream) -> None:
@@ -354,6 +361,19 @@ def osk_attention_masked(problem: Problem, q, k_pages, v_pages, mask, tau: float
     if ls is not None:
         res["lse"] = ls
     return res
+
+
+def union_order(problem: Problem, order, count, *, union_kmax=None, stream=None):
+    """Block-union lists (one table per sequence and KV group, cut causally per
+    query block); returns dict(order, count)."""
+    import torch
+    d = problem.dims()
+    uk = d.max_nk if union_kmax is None else int(union_kmax)
+    uo = torch.empty((problem.c.batch, problem.c.h_kv, d.max_nq, uk), dtype=torch.int32, device=order.device)
+    uc = torch.empty(uo.shape[:3], dtype=torch.int32, device=order.device)
+    cosa_union_order(problem.c, order.data_ptr(), count.data_ptr(), int(order.shape[3]), uo.data_ptr(),
+                     uc.data_ptr(), uk, _stream(stream))
+    return {"order": uo, "count": uc}
 
 
 def block_mass(problem: Problem, q, k_pages, lse, *, stream=None):

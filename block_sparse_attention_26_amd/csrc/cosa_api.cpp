@@ -349,6 +349,33 @@ cosa_status cosa_mask_from_order(const cosa_problem* problem, const int32_t* ord
                              stream, true);
 }
 
+cosa_status cosa_union_order(const cosa_problem* problem, const int32_t* order, const int32_t* count,
+                             int32_t kmax, int32_t* union_order, int32_t* union_count,
+                             int32_t union_kmax, void* stream) {
+  cosa_status st = validate(problem);
+  if (st != COSA_OK) return st;
+  if (!order || !count || !union_order || !union_count)
+    return fail(COSA_ERR_INVALID_ARG, "order, count, union_order and union_count must be non-NULL");
+  if (kmax < 1 || union_kmax < 1)
+    return fail(COSA_ERR_INVALID_ARG, "kmax and union_kmax must be >= 1 (got %d, %d)", kmax, union_kmax);
+  if (min_mask_words(problem) > 64)
+    return fail(COSA_ERR_UNSUPPORTED, "more than 4096 KV blocks per sequence");
+  cosa_dims_t d;
+  compute_dims(problem, 0, 0.0, &d);
+  cosa::MaskArgs a{};
+  a.seq = seq_args(problem, d);
+  a.block = problem->block;
+  a.n_rows = (int64_t)problem->batch * problem->h_kv * d.max_nq;
+  if (a.n_rows == 0) return ok();
+  a.kmax = kmax;
+  a.order = order;
+  a.count = count;
+  a.order_out = union_order;
+  a.count_out = union_count;
+  a.kmax_out = union_kmax;
+  return hip_result(cosa::launch_union_order(a, (hipStream_t)stream), "union-order launch");
+}
+
 cosa_status cosa_block_mass(const cosa_problem* problem, const void* q, const void* k_pages,
                             const float* lse, float* mass, void* stream) {
   cosa_status st = validate(problem);

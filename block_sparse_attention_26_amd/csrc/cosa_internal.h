@@ -80,6 +80,7 @@ struct MaskArgs {
   const uint64_t* mask_in;   // mask -> list input (null: every causal block)
   int32_t* order_out;
   int32_t* count_out;
+  int32_t kmax_out;          // union tables: width of order_out
 };
 
 // Exact block attention mass (one workgroup per batch * h_q * max_nq unit).
@@ -101,6 +102,7 @@ hipError_t launch_osk_bf16(const OskArgs& a, int head_dim, int block, bool dense
 hipError_t launch_kap(const KapArgs& a, int dtype, int head_dim, int block, hipStream_t stream);
 hipError_t launch_mask_from_order(const MaskArgs& a, hipStream_t stream);
 hipError_t launch_order_from_mask(const MaskArgs& a, hipStream_t stream);
+hipError_t launch_union_order(const MaskArgs& a, hipStream_t stream);
 hipError_t launch_block_mass(const MassArgs& a, int head_dim, int block, hipStream_t stream);
 
 }  // namespace cosa

@@ -87,7 +87,73 @@ __global__ __launch_bounds__(256) void order_from_mask_kernel(MaskArgs a) {
   if (lane == 0) a.count_out[row] = n_out;
 }
 
+// Block-union tables (CompactAttention page, selection stage): for a
+// (sequence, KV group), OR the listed causal blocks of all its query blocks
+// into one table, then write, for every query block, the table's blocks that
+// are causal for it, ascending. Each of kUnionSlices workgroups of a
+// (sequence, KV group) builds the table (a cheap pass over the lists) and
+// writes every kUnionSlices-th query block's list.
+constexpr int kUnionSlices = 16;
+
+__global__ __launch_bounds__(256) void union_order_kernel(MaskArgs a) {
+  __shared__ unsigned long long u[64];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int64_t bg = blockIdx.x / kUnionSlices;  // b * h_kv + g
+  const int slice = blockIdx.x % kUnionSlices;
+  const SeqArgs& sq = a.seq;
+  const int b = (int)(bg / sq.h_kv);
+  const int q0 = sq.cu_seqlens_q[b];
+  const int Lq = sq.cu_seqlens_q[b + 1] - q0;
+  const int Lk = sq.seqlens_k[b];
+  const int nq = (Lq + a.block - 1) / a.block;  // query blocks of this sequence
+  auto n_of = [&](int qb) { return (Lk - Lq + min(qb * a.block + a.block - 1, Lq - 1)) / a.block + 1; };
+  const int64_t row0 = bg * sq.max_nq;
+  if (tid < 64) u[tid] = 0ull;
+  __syncthreads();
+  for (int64_t i = tid; i < (int64_t)nq * a.kmax; i += 256) {
+    const int qb = (int)(i / a.kmax), t = (int)(i % a.kmax);
+    const int cnt = max(0, min(a.count[row0 + qb], a.kmax));
+    if (t >= cnt) continue;
+    const int kb = a.order[(row0 + qb) * a.kmax + t];
+    if (kb >= 0 && kb < n_of(qb)) atomicOr(&u[kb >> 6], 1ull << (kb & 63));
+  }
+  __syncthreads();
+  for (int qb = slice + kUnionSlices * w; qb < sq.max_nq; qb += kUnionSlices * 4) {
+    const int64_t row = row0 + qb;
+    const int n = qb < nq ? n_of(qb) : 0;
+    uint64_t bits = 0;
+    const int base = lane * 64;
+    if (base < n) {
+      bits = u[lane];
+      if (n - base < 64) bits &= (1ull << (n - base)) - 1ull;
+    }
+    const int pc = __popcll(bits);
+    int incl = pc;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += y;
+    }
+    const int total = __shfl(incl, 63, 64);
+    const int n_out = min(total, a.kmax_out);
+    int pos = incl - pc;
+    int32_t* lst = a.order_out + row * a.kmax_out;
+    while (bits && pos < n_out) {
+      lst[pos++] = base + __builtin_ctzll(bits);
+      bits &= bits - 1ull;
+    }
+    for (int t = n_out + lane; t < a.kmax_out; t += 64) lst[t] = -1;
+    if (lane == 0) a.count_out[row] = n_out;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_union_order(const MaskArgs& a, hipStream_t stream) {
+  const int64_t grid = (int64_t)a.seq.batch * a.seq.h_kv * kUnionSlices;
+  hipLaunchKernelGGL(union_order_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_mask_from_order(const MaskArgs& a, hipStream_t stream) {
   const int64_t grid = (a.n_rows + 3) / 4;

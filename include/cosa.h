@@ -236,6 +236,21 @@ cosa_status cosa_osk_attention_masked(const cosa_problem* problem, const void* q
                                       float skip_threshold, void* o, int32_t* visited,
                                       int32_t* skipped, float* lse, void* stream);
 
+/* Block-union tables for chunked prefill (CompactAttention page, selection
+ * stage: a union over the query blocks of the chunk, on top of the union over
+ * the query heads of a KV group that the lists already are; execution stage:
+ * a dense paged walk over the table). For each (b, g) the table is the set of
+ * causal blocks listed by any query block of the sequence; each query block
+ * gets the table's blocks that are causal for it, ascending, in
+ * union_order[b, g, qb, 0 .. union_count-1] (-1 pad, truncated to
+ * union_kmax; union_kmax >= max_nk never truncates). Walking these lists
+ * with cosa_osk_attention and skip_threshold 0 is the union method's
+ * execution; every block any query block selected stays covered.
+ * Limits: max_nk <= 4096. */
+cosa_status cosa_union_order(const cosa_problem* problem, const int32_t* order,
+                             const int32_t* count, int32_t kmax, int32_t* union_order,
+                             int32_t* union_count, int32_t union_kmax, void* stream);
+
 /* Exact attention mass of every causal block, the ranking of the oracle
  * selector on the COBS page ("Oracle Sparse Attention": keep the blocks that
  * hold the most exact softmax mass), against which a proxy's selection can be

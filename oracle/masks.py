@@ -1,4 +1,5 @@
-"""Binary block masks and exact attention mass (test infrastructure only).
+"""Binary block masks, block-union tables and exact attention mass (test
+infrastructure only).
 
 The CoSA summary contrasts its computation-order list with the binary masks
 of earlier proxies (§2.1, "Computation-Order Mask"; §1, proxy-driven methods)
@@ -24,6 +25,12 @@ R26 Exact block mass of (head h, query block qb, KV block kb): the dense
 R27 Recall of a selection for row (g, qb): its share of the row's group
     mass. The oracle selector at the same list length k keeps the k blocks of
     largest mass, so its recall bounds every selection of k blocks.
+R29 Block union (CompactAttention page, selection stage): the per-group lists
+    are already a union over the group's query heads; the Q-block union joins
+    the lists of all query blocks of a sequence into one table per (sequence,
+    KV group). Execution (the same page, zero-copy paged attention) walks the
+    table for every query block, each block cut to what is causal for it, in
+    ascending order.
 """
 from __future__ import annotations
 
@@ -65,6 +72,32 @@ def order_from_mask(mask, n_causal, kmax: int):
         order[idx + (slice(0, len(sel)),)] = sel
         count[idx] = len(sel)
     return order, count
+
+
+def union_lists(order, count, n_causal, kmax_out: int):
+    """Block-union lists (R29): for every (sequence, KV group) the union of the
+    causal blocks listed by its query blocks; each query block gets the union's
+    blocks that are causal for it, ascending, truncated to kmax_out.
+
+    order [batch, h_kv, nq, kmax], count / n_causal [batch, h_kv, nq].
+    Returns (order [batch, h_kv, nq, kmax_out] int32 with -1 pad, count)."""
+    order = np.asarray(order)
+    nb, hkv, nq, kmax = order.shape
+    out = np.full((nb, hkv, nq, kmax_out), -1, dtype=np.int32)
+    cnt = np.zeros((nb, hkv, nq), dtype=np.int32)
+    for b in range(nb):
+        for g in range(hkv):
+            union = set()
+            for qb in range(nq):
+                n = int(n_causal[b, g, qb])
+                c = max(0, min(int(count[b, g, qb]), kmax))
+                union.update(int(kb) for kb in order[b, g, qb, :c] if 0 <= kb < n)
+            for qb in range(nq):
+                n = int(n_causal[b, g, qb])
+                sel = sorted(kb for kb in union if kb < n)[:kmax_out]
+                out[b, g, qb, : len(sel)] = sel
+                cnt[b, g, qb] = len(sel)
+    return out, cnt
 
 
 def pack_words(mask, mask_words: int) -> np.ndarray:

@@ -177,3 +177,18 @@ def test_block_mass_rejects_bad_arguments():
     with pytest.raises(cosa.CosaError) as e:
         cosa.cosa_block_mass(f32.c, ptr, ptr, ptr, ptr, None)
     assert e.value.status == -2
+
+
+def test_union_order_rejects_bad_arguments():
+    _lib_or_skip()
+    p = _problem((2048,))
+    ptr = FakeDev(1, 16).data_ptr()
+    for args in [(None, ptr, 4, ptr, ptr, 16), (ptr, ptr, 0, ptr, ptr, 16), (ptr, ptr, 4, ptr, ptr, 0),
+                 (ptr, ptr, 4, None, ptr, 16)]:
+        with pytest.raises(cosa.CosaError) as e:
+            cosa.cosa_union_order(p.c, *args, None)
+        assert e.value.status == -1, args
+    big = _problem((1024,), (4097 * 128,))
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_union_order(big.c, ptr, ptr, 4, ptr, ptr, 16, None)
+    assert e.value.status == -2

@@ -173,3 +173,25 @@ def test_block_mass_parity(run):
     best = om.oracle_recall(Mg, run["ko"]["count"])
     live = np.isfinite(rec)
     assert (rec[live] <= best[live] + 1e-6).all()
+
+
+def test_union_order_exact_and_walk(run):
+    case, dev, ko = run["case"], run["dev"], run["ko"]
+    order = torch.from_numpy(ko["order"]).cuda()
+    count = torch.from_numpy(ko["count"]).cuda()
+    for uk in (run["max_nk"], 3):
+        say(run["name"], "union order, width", uk)
+        u = cosa.union_order(dev.problem, order, count, union_kmax=uk)
+        want_o, want_c = om.union_lists(ko["order"], ko["count"], run["n"], uk)
+        np.testing.assert_array_equal(u["order"].cpu().numpy(), want_o)
+        np.testing.assert_array_equal(u["count"].cpu().numpy(), want_c)
+    # the union walk (dense over the table, no skip) against the oracle's walk
+    say(run["name"], "union walk")
+    u = cosa.union_order(dev.problem, order, count)
+    g = cosa.osk_attention(dev.problem, dev.q, dev.k, dev.v, u["order"], u["count"], 0.0)
+    torch.cuda.synchronize()
+    uo, uc = u["order"].cpu().numpy(), u["count"].cpu().numpy()
+    ref = oc.osk_case(case, uo, uc, tau=0.0)
+    check_output(g["O"], ref["O"], case.dtype, run["name"] + " union")
+    assert int(g["skipped"].sum()) == 0
+    np.testing.assert_array_equal(g["visited"].cpu().numpy(), np.repeat(uc, case.h_q // case.h_kv, axis=1))

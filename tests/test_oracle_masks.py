@@ -129,3 +129,37 @@ def test_recall_and_oracle_selection_by_brute_force():
     assert np.isnan(best[3])
     full = masks.recall(M[:1], np.array([[5, 4, 3, 2, 1, 0]]), np.array([6]))
     assert abs(full[0] - 1.0) < 1e-15
+
+
+def test_union_lists_by_hand():
+    # one sequence, one KV group, three query blocks with 2, 4 and 5 causal blocks
+    order = np.array([[[[1, 0, -1], [3, 0, -1], [4, 9, 2]]]])  # 9 is not causal for qb 2: ignored
+    count = np.array([[[2, 2, 3]]])
+    n = np.array([[[2, 4, 5]]])
+    out, cnt = masks.union_lists(order, count, n, 5)
+    # union {0, 1, 2, 3, 4}, cut causally per query block
+    assert out[0, 0].tolist() == [[0, 1, -1, -1, -1], [0, 1, 2, 3, -1], [0, 1, 2, 3, 4]]
+    assert cnt[0, 0].tolist() == [2, 4, 5]
+    out, cnt = masks.union_lists(order, count, n, 3)  # truncation keeps the lowest blocks
+    assert out[0, 0, 2].tolist() == [0, 1, 2] and cnt[0, 0].tolist() == [2, 3, 3]
+
+
+def test_union_lists_cover_and_stay_minimal():
+    rng = np.random.default_rng(11)
+    nb, hkv, nq, kmax = 2, 3, 6, 4
+    n = np.tile(np.arange(3, 3 + nq), (nb, hkv, 1))
+    order = np.full((nb, hkv, nq, kmax), -1)
+    count = np.minimum(rng.integers(1, kmax + 1, size=(nb, hkv, nq)), n)
+    for idx in np.ndindex(nb, hkv, nq):
+        order[idx][: count[idx]] = rng.choice(n[idx], count[idx], replace=False)
+    out, cnt = masks.union_lists(order, count, n, 16)
+    for b in range(nb):
+        for g in range(hkv):
+            listed = {int(x) for qb in range(nq) for x in order[b, g, qb, : count[b, g, qb]]}
+            for qb in range(nq):
+                got = out[b, g, qb, : cnt[b, g, qb]].tolist()
+                assert got == sorted(got) and all(kb < n[b, g, qb] for kb in got)
+                # coverage: what this row listed survives; minimality: nothing unlisted appears
+                assert set(order[b, g, qb, : count[b, g, qb]].tolist()) <= set(got)
+                assert set(got) <= listed
+                assert set(got) == {kb for kb in listed if kb < n[b, g, qb]}
