@@ -8,12 +8,12 @@ point raises.
 Low-level functions carry the C names (``cosa_kap_order``,
 ``cosa_osk_attention``, ``cosa_dense_attention``, ``cosa_mask_from_order``,
 ``cosa_order_from_mask``, ``cosa_osk_attention_masked``, ``cosa_block_mass``,
-``cosa_union_order``,
+``cosa_union_order``, ``cosa_osk_decode``, ``cosa_osk_decode_workspace_size``,
 ``cosa_validate``,
 ``cosa_dims``, ``cosa_kap_workspace_size``) and take integer device pointers.
 The ``Problem`` class and the ``kap_order`` / ``osk_attention`` /
 ``dense_attention`` / ``mask_from_order`` / ``order_from_mask`` /
-``osk_attention_masked`` / ``block_mass`` / ``union_order`` helpers accept torch tensors that already live on the
+``osk_attention_masked`` / ``block_mass`` / ``union_order`` / ``osk_decode`` helpers accept torch tensors that already live on the
 GPU and allocate the outputs with torch.
 """
 from __future__ import annotations
@@ -29,8 +29,9 @@ __all__ = [
     "cosa_osk_attention", "cosa_dense_attention", "cosa_status_string",
     "cosa_last_error", "cosa_version", "cosa_mask_from_order", "cosa_order_from_mask",
     "cosa_osk_attention_masked", "cosa_block_mass", "cosa_union_order",
+    "cosa_osk_decode", "cosa_osk_decode_workspace_size",
     "kap_order", "osk_attention", "dense_attention", "mask_from_order", "order_from_mask",
-    "osk_attention_masked", "mask_words_for", "block_mass", "union_order",
+    "osk_attention_masked", "mask_words_for", "block_mass", "union_order", "osk_decode",
     "COSA_F32", "COSA_BF16", "EXPORTED_SYMBOLS",
 ]
 
@@ -44,6 +45,7 @@ EXPORTED_SYMBOLS = (
     "cosa_osk_attention", "cosa_dense_attention", "cosa_status_string",
     "cosa_last_error", "cosa_version", "cosa_mask_from_order", "cosa_order_from_mask",
     "cosa_osk_attention_masked", "cosa_block_mass", "cosa_union_order",
+    "cosa_osk_decode", "cosa_osk_decode_workspace_size",
 )
 
 
@@ -100,6 +102,8 @@ def load():
         "cosa_osk_attention_masked": (i32, [P, vp, vp, vp, vp, i32, i32, f32, vp, vp, vp, vp, vp]),
         "cosa_block_mass": (i32, [P, vp, vp, vp, vp, vp]),
         "cosa_union_order": (i32, [P, vp, vp, i32, vp, vp, i32, vp]),
+        "cosa_osk_decode_workspace_size": (sz, [P, i32]),
+        "cosa_osk_decode": (i32, [P, vp, vp, vp, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, vp, sz, vp]),
         "cosa_status_string": (ctypes.c_char_p, [i32]),
         "cosa_last_error": (ctypes.c_char_p, []),
         "cosa_version": (i32, []),
@@ -179,6 +183,17 @@ def cosa_osk_attention_masked(problem, q, k_pages, v_pages, mask, mask_words, gr
     _check(load().cosa_osk_attention_masked(ctypes.byref(problem), q, k_pages, v_pages, mask,
                                             int(mask_words), int(group), float(skip_threshold), o,
                                             visited, skipped, lse, stream))
+
+
+def cosa_osk_decode_workspace_size(problem, n_splits) -> int:
+    return load().cosa_osk_decode_workspace_size(ctypes.byref(problem), int(n_splits))
+
+
+def cosa_osk_decode(problem, q, k_pages, v_pages, order, count, kmax, group, skip_threshold, n_splits,
+                    o, visited, skipped, lse, workspace, workspace_bytes, stream) -> None:
+    _check(load().cosa_osk_decode(ctypes.byref(problem), q, k_pages, v_pages, order, count, int(kmax),
+                                  int(group), float(skip_threshold), int(n_splits), o, visited, skipped,
+                                  lse, workspace, int(workspace_bytes), stream))
 
 
 def cosa_union_order(problem, order, count, kmax, union_order, union_count, union_kmax, stream) -> None:
@@ -357,6 +372,30 @@ def osk_attention_masked(problem: Problem, q, k_pages, v_pages, mask, tau: float
     cosa_osk_attention_masked(problem.c, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
                               mask.data_ptr(), int(mask.shape[3]), problem.group, tau, o.data_ptr(),
                               vis.data_ptr(), skp.data_ptr(), _ptr(ls), _stream(stream))
+    res = {"O": o, "visited": vis, "skipped": skp}
+    if ls is not None:
+        res["lse"] = ls
+    return res
+
+
+def osk_decode(problem: Problem, q, k_pages, v_pages, order, count, tau: float, n_splits: int, *,
+               lse: bool = False, out=None, workspace=None, stream=None):
+    """Decode step over the proxy's lists, split into n_splits segments;
+    returns dict(O, visited, skipped[, lse])."""
+    import torch
+    dev = q.device
+    d = problem.dims()
+    o = torch.empty_like(q) if out is None else out
+    vis = torch.empty((problem.c.batch, problem.c.h_q, d.max_nq), dtype=torch.int32, device=dev)
+    skp = torch.empty_like(vis)
+    ls = torch.empty((problem.c.h_q, d.total_q), dtype=torch.float32, device=dev) if lse else None
+    ws_bytes = cosa_osk_decode_workspace_size(problem.c, n_splits)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    cosa_osk_decode(problem.c, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), order.data_ptr(),
+                    count.data_ptr(), int(order.shape[3]), problem.group, tau, n_splits, o.data_ptr(),
+                    vis.data_ptr(), skp.data_ptr(), _ptr(ls), workspace.data_ptr(), workspace.numel(),
+                    _stream(stream))
     res = {"O": o, "visited": vis, "skipped": skp}
     if ls is not None:
         res["lse"] = ls

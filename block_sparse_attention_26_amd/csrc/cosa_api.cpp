@@ -115,6 +115,11 @@ size_t kap_ws_size(const cosa_problem* p, int pool, bool with_scores) {
   return sz;
 }
 
+size_t decode_ws_size(const cosa_problem* p, int n_splits) {
+  return align256((size_t)p->batch * p->h_q * n_splits * (p->head_dim + 2) * sizeof(float)) +
+         align256((size_t)p->batch * p->h_q * n_splits * 2 * sizeof(int32_t));
+}
+
 cosa::SeqArgs seq_args(const cosa_problem* p, const cosa_dims_t& d) {
   cosa::SeqArgs s;
   s.cu_seqlens_q = p->cu_seqlens_q;
@@ -374,6 +379,66 @@ cosa_status cosa_union_order(const cosa_problem* problem, const int32_t* order, 
   a.count_out = union_count;
   a.kmax_out = union_kmax;
   return hip_result(cosa::launch_union_order(a, (hipStream_t)stream), "union-order launch");
+}
+
+size_t cosa_osk_decode_workspace_size(const cosa_problem* problem, int32_t n_splits) {
+  if (validate(problem) != COSA_OK || n_splits < 1) return 0;
+  return decode_ws_size(problem, n_splits);
+}
+
+cosa_status cosa_osk_decode(const cosa_problem* problem, const void* q, const void* k_pages,
+                            const void* v_pages, const int32_t* order, const int32_t* count,
+                            int32_t kmax, int32_t group, float skip_threshold, int32_t n_splits,
+                            void* o, int32_t* visited, int32_t* skipped, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  cosa_status st = validate(problem);
+  if (st != COSA_OK) return st;
+  const cosa_problem* p = problem;
+  if (!q || !k_pages || !v_pages || !o || !order || !count || !visited || !skipped)
+    return fail(COSA_ERR_INVALID_ARG, "q, k_pages, v_pages, o, order, count, visited and skipped must be non-NULL");
+  if (p->dtype != COSA_BF16) return fail(COSA_ERR_UNSUPPORTED, "the decode walk is built for bf16 only");
+  if (kmax < 1) return fail(COSA_ERR_INVALID_ARG, "kmax must be >= 1 (got %d)", kmax);
+  if (group != p->h_q / p->h_kv)
+    return fail(COSA_ERR_INVALID_ARG, "group (%d) must equal h_q / h_kv (%d)", group, p->h_q / p->h_kv);
+  if (group > 32) return fail(COSA_ERR_UNSUPPORTED, "the decode walk handles up to 32 query heads per KV head");
+  if (!(skip_threshold >= 0.f && skip_threshold < 1.f))
+    return fail(COSA_ERR_INVALID_ARG, "skip_threshold must lie in [0, 1) (got %g)", (double)skip_threshold);
+  if (n_splits < 1 || n_splits > 1024)
+    return fail(COSA_ERR_INVALID_ARG, "n_splits must lie in [1, 1024] (got %d)", n_splits);
+  for (int b = 0; b < p->batch; ++b)
+    if (p->host_cu_seqlens_q[b + 1] - p->host_cu_seqlens_q[b] > 1)
+      return fail(COSA_ERR_INVALID_ARG, "sequence %d has %d query tokens; a decode step has at most one", b,
+                  p->host_cu_seqlens_q[b + 1] - p->host_cu_seqlens_q[b]);
+  const size_t need = decode_ws_size(p, n_splits);
+  if (!workspace || workspace_bytes < need)
+    return fail(COSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (((uintptr_t)workspace & 255) != 0) return fail(COSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  cosa_dims_t d;
+  compute_dims(p, 0, 0.0, &d);
+  if (d.total_q == 0 || d.max_nq == 0) return ok();
+  cosa::DecodeArgs a{};
+  a.seq = seq_args(p, d);
+  a.q = q;
+  a.k = k_pages;
+  a.v = v_pages;
+  a.o = o;
+  a.order = order;
+  a.count = count;
+  a.visited = visited;
+  a.skipped = skipped;
+  a.lse = lse;
+  unsigned char* ws = (unsigned char*)workspace;
+  a.part = (float*)ws;
+  ws += align256((size_t)p->batch * p->h_q * n_splits * (p->head_dim + 2) * sizeof(float));
+  a.part_counts = (int32_t*)ws;
+  a.total_q = d.total_q;
+  a.kmax = kmax;
+  a.n_splits = n_splits;
+  a.scale = p->softmax_scale;
+  a.scale_log2 = (float)((double)p->softmax_scale * 1.4426950408889634);
+  a.skip_on = skip_threshold > 0.f ? 1 : 0;
+  a.skip_thr_raw = a.skip_on ? (float)(log((double)skip_threshold) / (double)p->softmax_scale) : 0.f;
+  return hip_result(cosa::launch_osk_decode(a, p->head_dim, p->block, (hipStream_t)stream), "decode launch");
 }
 
 cosa_status cosa_block_mass(const cosa_problem* problem, const void* q, const void* k_pages,

@@ -95,6 +95,30 @@ struct MassArgs {
   int64_t n_units;
 };
 
+// Decode-stage walk: one workgroup per (sequence, KV group, list segment),
+// then one wave per (sequence, query head) merging the segments.
+struct DecodeArgs {
+  SeqArgs seq;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const int32_t* order;    // [batch, h_kv, max_nq (= 1), kmax]
+  const int32_t* count;    // [batch, h_kv, max_nq]
+  int32_t* visited;        // [batch, h_q, max_nq]
+  int32_t* skipped;        // [batch, h_q, max_nq]
+  float* lse;              // [h_q, total_q] (nullable)
+  float* part;             // [batch, h_q, n_splits, D + 2]: acc, running max, sum
+  int32_t* part_counts;    // [batch, h_q, n_splits, 2]: visited, skipped
+  int32_t total_q;
+  int32_t kmax;
+  int32_t n_splits;
+  float scale;
+  float scale_log2;
+  float skip_thr_raw;
+  int32_t skip_on;
+};
+
 // Each launcher returns hipSuccess or the launch error. `dtype` is cosa_dtype.
 hipError_t launch_osk(const OskArgs& a, int dtype, int head_dim, int block, bool dense,
                       hipStream_t stream);
@@ -104,5 +128,6 @@ hipError_t launch_mask_from_order(const MaskArgs& a, hipStream_t stream);
 hipError_t launch_order_from_mask(const MaskArgs& a, hipStream_t stream);
 hipError_t launch_union_order(const MaskArgs& a, hipStream_t stream);
 hipError_t launch_block_mass(const MassArgs& a, int head_dim, int block, hipStream_t stream);
+hipError_t launch_osk_decode(const DecodeArgs& a, int head_dim, int block, hipStream_t stream);
 
 }  // namespace cosa

@@ -193,6 +193,31 @@ cosa_status cosa_osk_attention(const cosa_problem* problem, const void* q, const
 cosa_status cosa_dense_attention(const cosa_problem* problem, const void* q, const void* k_pages,
                                  const void* v_pages, void* o, float* lse, void* stream);
 
+/* ---- Decode step ---------------------------------------------------------------
+ * One new query token per sequence (cu_seqlens_q steps of 0 or 1; the token
+ * sits at absolute position seqlens_k[b] - 1, its key and value already in
+ * the cache). The pages name decoding as future work without a method; this
+ * keeps the walk of cosa_osk_attention (listed pages only, list order, skip
+ * per query head) and splits each (b, g) list into n_splits contiguous
+ * segments, entries [floor(s*n/S), floor((s+1)*n/S)), walked by separate
+ * workgroups from an empty state (so a segment's first block is never
+ * skipped) and merged exactly by log-sum-exp. With skip_threshold 0 the
+ * result is softmax attention over the listed keys for every n_splits.
+ *  order, count  the proxy's lists for the single query block (cosa_kap_order
+ *                on the decode problem), kmax their width.
+ *  o             [total_q, h_q, head_dim] bf16; visited / skipped
+ *                [batch, h_q, 1] summed over the segments; lse as in
+ *                cosa_osk_attention (nullable).
+ *  workspace     cosa_osk_decode_workspace_size(problem, n_splits) bytes,
+ *                256-byte aligned (per-segment partial results).
+ * bf16 only; G = h_q / h_kv <= 32; 1 <= n_splits <= 1024. */
+size_t cosa_osk_decode_workspace_size(const cosa_problem* problem, int32_t n_splits);
+cosa_status cosa_osk_decode(const cosa_problem* problem, const void* q, const void* k_pages,
+                            const void* v_pages, const int32_t* order, const int32_t* count,
+                            int32_t kmax, int32_t group, float skip_threshold, int32_t n_splits,
+                            void* o, int32_t* visited, int32_t* skipped, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- Binary block masks (comparison modes) -----------------------------------
  * The CoSA summary contrasts its computation-order list (§2.1) with the
  * binary masks of earlier proxies, and its page-remapped walk (§2.3,

@@ -31,9 +31,12 @@ Modules:
     kap    - the Kernel-Aware Proxy: pooling, proxy scores, MaxNorm, HRM,
              flag-grouped sort and budget truncation.
     osk    - ordered online-softmax accumulation with the in-kernel skip rule.
-    masks  - binary block masks <-> ascending lists, exact block attention
-             mass and the recall of a selection (comparison modes).
+    masks  - binary block masks <-> ascending lists, block-union tables,
+             exact block attention mass and the recall of a selection
+             (comparison modes).
+    decode - the decode-stage walk: one query token, the list cut into
+             segments walked separately and merged by log-sum-exp.
     layout - causal block arithmetic and page gathering used by the above.
     cases  - convenience wrappers that run the oracle on a whole packed batch.
 """
-from . import exp32, dense, kap, osk, masks, layout, cases  # noqa: F401
+from . import exp32, dense, kap, osk, masks, decode, layout, cases  # noqa: F401

@@ -192,3 +192,29 @@ def test_union_order_rejects_bad_arguments():
     with pytest.raises(cosa.CosaError) as e:
         cosa.cosa_union_order(big.c, ptr, ptr, 4, ptr, ptr, 16, None)
     assert e.value.status == -2
+
+
+def test_decode_rejects_bad_arguments():
+    _lib_or_skip()
+    p = _problem((1, 1, 1), (5000, 700, 9000))
+    ptr = FakeDev(1, 16).data_ptr()
+    need = cosa.cosa_osk_decode_workspace_size(p.c, 4)
+    assert need == ((3 * 32 * 4 * 130 * 4 + 255) // 256) * 256 + ((3 * 32 * 4 * 2 * 4 + 255) // 256) * 256
+    assert cosa.cosa_osk_decode_workspace_size(p.c, 0) == 0
+    base = dict(kmax=4, group=4, tau=1e-7, S=4, ws=ptr, wsb=1 << 30)
+    for bad, status in [(dict(kmax=0), -1), (dict(group=3), -1), (dict(tau=1.0), -1), (dict(S=0), -1),
+                        (dict(S=2000), -1), (dict(wsb=16), -3)]:
+        args = dict(base)
+        args.update(bad)
+        with pytest.raises(cosa.CosaError) as e:
+            cosa.cosa_osk_decode(p.c, ptr, ptr, ptr, ptr, ptr, args["kmax"], args["group"], args["tau"], args["S"],
+                                 ptr, ptr, ptr, None, args["ws"], args["wsb"], None)
+        assert e.value.status == status, bad
+    prefill = _problem((64,), (5000,))  # more than one query token
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_osk_decode(prefill.c, ptr, ptr, ptr, ptr, ptr, 4, 4, 0.0, 1, ptr, ptr, ptr, None, ptr, 1 << 30, None)
+    assert e.value.status == -1
+    wide = _problem((1,), (5000,), h_q=64, h_kv=1)  # 64 query heads per KV head
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_osk_decode(wide.c, ptr, ptr, ptr, ptr, ptr, 4, 64, 0.0, 1, ptr, ptr, ptr, None, ptr, 1 << 30, None)
+    assert e.value.status == -2
