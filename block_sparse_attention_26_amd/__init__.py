@@ -9,11 +9,12 @@ Low-level functions carry the C names (``cosa_kap_order``,
 ``cosa_osk_attention``, ``cosa_dense_attention``, ``cosa_mask_from_order``,
 ``cosa_order_from_mask``, ``cosa_osk_attention_masked``, ``cosa_block_mass``,
 ``cosa_union_order``, ``cosa_osk_decode``, ``cosa_osk_decode_workspace_size``,
+``cosa_kap_rank``, ``cosa_cobs_scores``, ``cosa_cobs_workspace_size``,
 ``cosa_validate``,
 ``cosa_dims``, ``cosa_kap_workspace_size``) and take integer device pointers.
 The ``Problem`` class and the ``kap_order`` / ``osk_attention`` /
 ``dense_attention`` / ``mask_from_order`` / ``order_from_mask`` /
-``osk_attention_masked`` / ``block_mass`` / ``union_order`` / ``osk_decode`` helpers accept torch tensors that already live on the
+``osk_attention_masked`` / ``block_mass`` / ``union_order`` / ``osk_decode`` / ``kap_rank`` / ``cobs_scores`` helpers accept torch tensors that already live on the
 GPU and allocate the outputs with torch.
 """
 from __future__ import annotations
@@ -29,9 +30,11 @@ __all__ = [
     "cosa_osk_attention", "cosa_dense_attention", "cosa_status_string",
     "cosa_last_error", "cosa_version", "cosa_mask_from_order", "cosa_order_from_mask",
     "cosa_osk_attention_masked", "cosa_block_mass", "cosa_union_order",
-    "cosa_osk_decode", "cosa_osk_decode_workspace_size",
+    "cosa_osk_decode", "cosa_osk_decode_workspace_size", "cosa_kap_rank", "cosa_cobs_scores",
+    "cosa_cobs_workspace_size",
     "kap_order", "osk_attention", "dense_attention", "mask_from_order", "order_from_mask",
-    "osk_attention_masked", "mask_words_for", "block_mass", "union_order", "osk_decode",
+    "osk_attention_masked", "mask_words_for", "block_mass", "union_order", "osk_decode", "kap_rank",
+    "cobs_scores",
     "COSA_F32", "COSA_BF16", "EXPORTED_SYMBOLS",
 ]
 
@@ -45,7 +48,8 @@ EXPORTED_SYMBOLS = (
     "cosa_osk_attention", "cosa_dense_attention", "cosa_status_string",
     "cosa_last_error", "cosa_version", "cosa_mask_from_order", "cosa_order_from_mask",
     "cosa_osk_attention_masked", "cosa_block_mass", "cosa_union_order",
-    "cosa_osk_decode", "cosa_osk_decode_workspace_size",
+    "cosa_osk_decode", "cosa_osk_decode_workspace_size", "cosa_kap_rank", "cosa_cobs_scores",
+    "cosa_cobs_workspace_size",
 )
 
 
@@ -103,6 +107,9 @@ def load():
         "cosa_block_mass": (i32, [P, vp, vp, vp, vp, vp]),
         "cosa_union_order": (i32, [P, vp, vp, i32, vp, vp, i32, vp]),
         "cosa_osk_decode_workspace_size": (sz, [P, i32]),
+        "cosa_kap_rank": (i32, [P, i32, f64, vp, vp, vp, vp, i32, vp, vp]),
+        "cosa_cobs_workspace_size": (sz, [P, i32]),
+        "cosa_cobs_scores": (i32, [P, vp, vp, i32, vp, vp, sz, vp]),
         "cosa_osk_decode": (i32, [P, vp, vp, vp, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, vp, sz, vp]),
         "cosa_status_string": (ctypes.c_char_p, [i32]),
         "cosa_last_error": (ctypes.c_char_p, []),
@@ -183,6 +190,20 @@ def cosa_osk_attention_masked(problem, q, k_pages, v_pages, mask, mask_words, gr
     _check(load().cosa_osk_attention_masked(ctypes.byref(problem), q, k_pages, v_pages, mask,
                                             int(mask_words), int(group), float(skip_threshold), o,
                                             visited, skipped, lse, stream))
+
+
+def cosa_kap_rank(problem, pool, budget, scores, order, hrm, count, kmax, block_scores, stream) -> None:
+    _check(load().cosa_kap_rank(ctypes.byref(problem), int(pool), float(budget), scores, order, hrm, count,
+                                int(kmax), block_scores, stream))
+
+
+def cosa_cobs_workspace_size(problem, pool) -> int:
+    return load().cosa_cobs_workspace_size(ctypes.byref(problem), int(pool))
+
+
+def cosa_cobs_scores(problem, q, k_pages, pool, scores, workspace, workspace_bytes, stream) -> None:
+    _check(load().cosa_cobs_scores(ctypes.byref(problem), q, k_pages, int(pool), scores, workspace,
+                                   int(workspace_bytes), stream))
 
 
 def cosa_osk_decode_workspace_size(problem, n_splits) -> int:
@@ -376,6 +397,39 @@ def osk_attention_masked(problem: Problem, q, k_pages, v_pages, mask, tau: float
     if ls is not None:
         res["lse"] = ls
     return res
+
+
+def kap_rank(problem: Problem, scores, pool: int, budget: float, *, kmax=None, export_block_scores=False,
+             stream=None):
+    """Rank/sort pass over given scores; returns dict(order, hrm, count, kmax[, s])."""
+    import torch
+    dev = scores.device
+    d = problem.dims(pool, budget)
+    kmax = d.kmax if kmax is None else int(kmax)
+    order = torch.empty((problem.c.batch, problem.c.h_kv, d.max_nq, kmax), dtype=torch.int32, device=dev)
+    hrm = torch.empty(order.shape, dtype=torch.uint8, device=dev)
+    count = torch.empty(order.shape[:3], dtype=torch.int32, device=dev)
+    s = (torch.empty((problem.c.batch, problem.c.h_kv, d.max_nq, d.max_nk), dtype=torch.float32, device=dev)
+         if export_block_scores else None)
+    cosa_kap_rank(problem.c, pool, budget, scores.data_ptr(), order.data_ptr(), hrm.data_ptr(),
+                  count.data_ptr(), kmax, _ptr(s), _stream(stream))
+    out = {"order": order, "hrm": hrm, "count": count, "kmax": kmax}
+    if s is not None:
+        out["s"] = s
+    return out
+
+
+def cobs_scores(problem: Problem, q, k_pages, pool: int, *, workspace=None, stream=None):
+    """Second-order block scores [batch, h_q, max_nr, max_nk] fp32."""
+    import torch
+    d = problem.dims(pool, 0.0)
+    out = torch.empty((problem.c.batch, problem.c.h_q, d.max_nr, d.max_nk), dtype=torch.float32, device=q.device)
+    ws_bytes = cosa_cobs_workspace_size(problem.c, pool)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    cosa_cobs_scores(problem.c, q.data_ptr(), k_pages.data_ptr(), pool, out.data_ptr(), workspace.data_ptr(),
+                     workspace.numel(), _stream(stream))
+    return out
 
 
 def osk_decode(problem: Problem, q, k_pages, v_pages, order, count, tau: float, n_splits: int, *,

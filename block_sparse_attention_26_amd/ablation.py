@@ -15,6 +15,9 @@ synthetic workload, all through the library's C ABI:
                 order as "ascending")
     skip-only   every causal block in ascending order, skip on (a fixed-order
                 kernel with in-kernel skipping and no proxy)
+    cobs        lists ranked by second-order block scores (the COBS page's
+                mean + half variance of a block's scores, exact covariance)
+                instead of max-pooled scores, HRM-first order, skip on
     union       the CompactAttention page's execution: the proxy lists of all
                 query blocks of a sequence joined into one table per KV group,
                 walked densely (ascending, causal cut, skip off)
@@ -43,7 +46,7 @@ import time
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 WORKLOADS = {"cfg1": 1, "cfg2": 2, "cfg3": 3, "cfg4": 4, "cfg5": 5}
-MODES = ("cosa", "kap-only", "ascending", "mask-scan", "skip-only", "union", "dense")
+MODES = ("cosa", "kap-only", "ascending", "mask-scan", "skip-only", "cobs", "union", "dense")
 
 
 def _log(*a):
@@ -115,6 +118,8 @@ def run(args) -> list:
     asc, asc_ms, _ = _timed(lambda: cosa.order_from_mask(pr, mask, d.kmax), reps, stream)
     full, full_ms, _ = _timed(lambda: cosa.order_from_mask(pr, None, d.max_nk, device=dev), reps, stream)
     uni, uni_ms, _ = _timed(lambda: cosa.union_order(pr, order, count), reps, stream)
+    P2, p2_ms, _ = _timed(lambda: cosa.cobs_scores(pr, q, k, case.pool), reps, stream)
+    kc, kc_ms, _ = _timed(lambda: cosa.kap_rank(pr, P2, case.pool, case.budget), reps, stream)
 
     walks = {
         "cosa": (lambda: cosa.osk_attention(pr, q, k, v, order, count, tau), kap_ms),
@@ -124,6 +129,7 @@ def run(args) -> list:
         "mask-scan": (lambda: cosa.osk_attention_masked(pr, q, k, v, mask, tau), kap_ms + mask_ms),
         "skip-only": (lambda: cosa.osk_attention(pr, q, k, v, full["order"], full["count"], tau), 0.0),
         "union": (lambda: cosa.osk_attention(pr, q, k, v, uni["order"], uni["count"], 0.0), kap_ms + uni_ms),
+        "cobs": (lambda: cosa.osk_attention(pr, q, k, v, kc["order"], kc["count"], tau), p2_ms + kc_ms),
     }
     rows = []
     for mode in MODES:
@@ -172,6 +178,9 @@ def run(args) -> list:
         live = (c > 0) & (tot > 0)
         rec = picked.sum(axis=-1)[live] / tot[live]
         best = top[live] / tot[live]
+        co = kc["order"].cpu().numpy().astype(np.int64)
+        cvalid = np.arange(co.shape[-1])[None, None, None, :] < kc["count"].cpu().numpy()[..., None]
+        crec = (np.take_along_axis(Mg, np.where(cvalid, co, 0), axis=-1) * cvalid).sum(axis=-1)[live] / tot[live]
         uo = uni["order"].cpu().numpy().astype(np.int64)
         uc = uni["count"].cpu().numpy()
         uvalid = np.arange(uo.shape[-1])[None, None, None, :] < uc[..., None]
@@ -183,13 +192,16 @@ def run(args) -> list:
             "oracle_recall_mean": float(best.mean()),
             "oracle_recall_min": float(best.min()),
             "union_recall_mean": float(urec.mean()),
+            "cobs_recall_mean": float(crec.mean()),
+            "cobs_recall_min": float(crec.min()),
             "rows": int(live.sum()),
             "seconds": time.perf_counter() - t0,
         }
         rows.append(summary)
         _log(f"mass recall: proxy {summary['kap_recall_mean']:.4f} (min {summary['kap_recall_min']:.4f}),"
              f" oracle top-k {summary['oracle_recall_mean']:.4f} (min {summary['oracle_recall_min']:.4f}),"
-             f" union {summary['union_recall_mean']:.4f}")
+             f" union {summary['union_recall_mean']:.4f}, second-order {summary['cobs_recall_mean']:.4f}"
+             f" (min {summary['cobs_recall_min']:.4f})")
 
     meta = {"workload": args.workload, "seq_len": case.seqlens_q if case.batch > 1 else case.seqlens_q[0],
             "h_q": case.h_q, "h_kv": case.h_kv, "head_dim": case.head_dim, "block": case.block,

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcosa.so")
-SOURCES = ["cosa_api.cpp", "osk.hip", "osk_bf16.hip", "kap.hip", "mask.hip", "mass.hip", "decode.hip"]
+SOURCES = ["cosa_api.cpp", "osk.hip", "osk_bf16.hip", "kap.hip", "mask.hip", "mass.hip", "decode.hip", "cobs.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

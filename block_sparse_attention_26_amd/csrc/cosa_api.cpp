@@ -381,6 +381,76 @@ cosa_status cosa_union_order(const cosa_problem* problem, const int32_t* order, 
   return hip_result(cosa::launch_union_order(a, (hipStream_t)stream), "union-order launch");
 }
 
+size_t cosa_cobs_workspace_size(const cosa_problem* problem, int32_t pool) {
+  if (validate(problem) != COSA_OK || check_pool(problem, pool) != COSA_OK) return 0;
+  cosa_dims_t d;
+  compute_dims(problem, pool, 0.0, &d);
+  return align256((size_t)problem->batch * d.max_nr * problem->h_q * problem->head_dim * 2);
+}
+
+cosa_status cosa_cobs_scores(const cosa_problem* problem, const void* q, const void* k_pages, int32_t pool,
+                             float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+  cosa_status st = validate(problem);
+  if (st != COSA_OK) return st;
+  if ((st = check_pool(problem, pool)) != COSA_OK) return st;
+  if (!q || !k_pages || !scores) return fail(COSA_ERR_INVALID_ARG, "q, k_pages and scores must be non-NULL");
+  if (problem->dtype != COSA_BF16) return fail(COSA_ERR_UNSUPPORTED, "second-order scores are built for bf16 only");
+  const size_t need = cosa_cobs_workspace_size(problem, pool);
+  if (!workspace || workspace_bytes < need)
+    return fail(COSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (((uintptr_t)workspace & 255) != 0) return fail(COSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  cosa_dims_t d;
+  compute_dims(problem, pool, 0.0, &d);
+  if (d.total_q == 0 || d.max_nr == 0) return ok();
+  cosa::KapArgs a{};
+  a.seq = seq_args(problem, d);
+  a.q = q;
+  a.k = k_pages;
+  a.q_pool = workspace;
+  a.scores = scores;
+  a.pool = pool;
+  a.max_nr = d.max_nr;
+  a.scale = problem->softmax_scale;
+  hipError_t e = cosa::launch_kap_pool_q(a, problem->dtype, problem->head_dim, (hipStream_t)stream);
+  if (e == hipSuccess) e = cosa::launch_cobs_scores(a, problem->head_dim, problem->block, (hipStream_t)stream);
+  return hip_result(e, "second-order score launch");
+}
+
+cosa_status cosa_kap_rank(const cosa_problem* problem, int32_t pool, double budget, const float* scores,
+                          int32_t* order, uint8_t* hrm, int32_t* count, int32_t kmax, float* block_scores,
+                          void* stream) {
+  cosa_status st = validate(problem);
+  if (st != COSA_OK) return st;
+  if ((st = check_pool(problem, pool)) != COSA_OK) return st;
+  if (!(budget > 0.0 && budget <= 1.0))
+    return fail(COSA_ERR_INVALID_ARG, "budget must lie in (0, 1] (got %g)", budget);
+  if (!scores || !order || !hrm || !count)
+    return fail(COSA_ERR_INVALID_ARG, "scores, order, hrm and count must be non-NULL");
+  cosa_dims_t d;
+  compute_dims(problem, pool, budget, &d);
+  if (kmax < d.kmax)
+    return fail(COSA_ERR_INVALID_ARG, "kmax (%d) is smaller than the widest list (%d)", kmax, d.kmax);
+  if (d.max_nk > cosa::kMaxSortBlocks)
+    return fail(COSA_ERR_UNSUPPORTED, "max KV blocks per sequence %d exceeds %d", d.max_nk, cosa::kMaxSortBlocks);
+  if ((int64_t)(problem->h_q / problem->h_kv) * (problem->block / pool) > 4096)
+    return fail(COSA_ERR_UNSUPPORTED, "group * block / pool exceeds 4096 pooled rows per list");
+  if (d.total_q == 0 || d.max_nq == 0) return ok();
+  cosa::KapArgs a{};
+  a.seq = seq_args(problem, d);
+  a.scores = const_cast<float*>(scores);  // read only
+  a.row_max = nullptr;                    // the rank pass takes the row maxima itself
+  a.block_scores = block_scores;
+  a.order = order;
+  a.hrm = hrm;
+  a.count = count;
+  a.pool = pool;
+  a.max_nr = d.max_nr;
+  a.kmax = kmax;
+  a.budget = budget;
+  a.scale = problem->softmax_scale;
+  return hip_result(cosa::launch_kap_rank(a, problem->block, (hipStream_t)stream), "rank launch");
+}
+
 size_t cosa_osk_decode_workspace_size(const cosa_problem* problem, int32_t n_splits) {
   if (validate(problem) != COSA_OK || n_splits < 1) return 0;
   return decode_ws_size(problem, n_splits);

@@ -124,6 +124,10 @@ hipError_t launch_osk(const OskArgs& a, int dtype, int head_dim, int block, bool
                       hipStream_t stream);
 hipError_t launch_osk_bf16(const OskArgs& a, int head_dim, int block, bool dense, hipStream_t stream);
 hipError_t launch_kap(const KapArgs& a, int dtype, int head_dim, int block, hipStream_t stream);
+// single stages: query pooling (bf16) and the rank/sort pass over given scores
+hipError_t launch_kap_pool_q(const KapArgs& a, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_kap_rank(const KapArgs& a, int block, hipStream_t stream);
+hipError_t launch_cobs_scores(const KapArgs& a, int head_dim, int block, hipStream_t stream);
 hipError_t launch_mask_from_order(const MaskArgs& a, hipStream_t stream);
 hipError_t launch_order_from_mask(const MaskArgs& a, hipStream_t stream);
 hipError_t launch_union_order(const MaskArgs& a, hipStream_t stream);

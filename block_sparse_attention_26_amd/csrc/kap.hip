@@ -595,6 +595,28 @@ hipError_t launch_all(const KapArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t launch_kap_pool_q(const KapArgs& a, int dtype, int head_dim, hipStream_t stream) {
+  const int64_t g1 = (int64_t)a.seq.batch * a.max_nr;
+  if (dtype == 1 && head_dim == 128)
+    hipLaunchKernelGGL((kap_pool_q<true, 128>), dim3((unsigned)g1), dim3(kThreads), 0, stream, a);
+  else if (dtype == 1 && head_dim == 64)
+    hipLaunchKernelGGL((kap_pool_q<true, 64>), dim3((unsigned)g1), dim3(kThreads), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_kap_rank(const KapArgs& a, int block, hipStream_t stream) {
+  const int64_t g4 = (int64_t)a.seq.max_nq * a.seq.batch * a.seq.h_kv;
+  if (block == 128)
+    hipLaunchKernelGGL((kap_rank_sort<128>), dim3((unsigned)g4), dim3(kThreads), 0, stream, a);
+  else if (block == 64)
+    hipLaunchKernelGGL((kap_rank_sort<64>), dim3((unsigned)g4), dim3(kThreads), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_kap(const KapArgs& a, int dtype, int head_dim, int block, hipStream_t stream) {
   const bool bf = dtype == 1;
 #define COSA_KAP_CASE(BF, DD, BB) \

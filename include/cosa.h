@@ -193,6 +193,32 @@ cosa_status cosa_osk_attention(const cosa_problem* problem, const void* q, const
 cosa_status cosa_dense_attention(const cosa_problem* problem, const void* q, const void* k_pages,
                                  const void* v_pages, void* o, float* lse, void* stream);
 
+/* ---- Ranking from given scores; second-order scores ---------------------------
+ * cosa_kap_rank runs the proxy's MaxNorm, HRM flags, sort and budget (as in
+ * cosa_kap_order, bit for bit) on a caller's score tensor
+ * scores fp32 [batch, h_q, max_nr, max_nk] (-inf where a pooled row sees no
+ * key of a block), so any block score can drive the computation order.
+ * Limits as cosa_kap_order. */
+cosa_status cosa_kap_rank(const cosa_problem* problem, int32_t pool, double budget,
+                          const float* scores, int32_t* order, uint8_t* hrm, int32_t* count,
+                          int32_t kmax, float* block_scores, void* stream);
+
+/* Second-order block scores (COBS page §2.2-2.3: rank blocks by the first two
+ * cumulants of their log attention mass, q.k_mean + 1/2 q^T Sigma q). For
+ * pooled query row r (mean of p queries, as in cosa_kap_order) and KV block
+ * kb, with s_j = softmax_scale * q_pooled[r] . k_j over the raw keys j of kb
+ * that the row's window may see (j <= off + min(r*p+p-1, Lq-1)):
+ *   scores[b, h, r, kb] = mean_j s_j + 1/2 var_j s_j   (population variance)
+ * i.e. the page's score with the exact per-block key mean and covariance, no
+ * compression; -inf where no key is visible and in all padding. It costs a
+ * (pooled rows x keys) product per head, B/p times the max-pooled score's.
+ * workspace: cosa_cobs_workspace_size bytes (pooled queries), 256-byte
+ * aligned. bf16 only. */
+size_t cosa_cobs_workspace_size(const cosa_problem* problem, int32_t pool);
+cosa_status cosa_cobs_scores(const cosa_problem* problem, const void* q, const void* k_pages,
+                             int32_t pool, float* scores, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* ---- Decode step ---------------------------------------------------------------
  * One new query token per sequence (cu_seqlens_q steps of 0 or 1; the token
  * sits at absolute position seqlens_k[b] - 1, its key and value already in

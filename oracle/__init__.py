@@ -36,7 +36,9 @@ Modules:
              (comparison modes).
     decode - the decode-stage walk: one query token, the list cut into
              segments walked separately and merged by log-sum-exp.
+    cobs   - second-order block scores (mean + half variance of the scores
+             over a block's keys) as an alternative proxy ranking.
     layout - causal block arithmetic and page gathering used by the above.
     cases  - convenience wrappers that run the oracle on a whole packed batch.
 """
-from . import exp32, dense, kap, osk, masks, decode, layout, cases  # noqa: F401
+from . import exp32, dense, kap, osk, masks, decode, cobs, layout, cases  # noqa: F401

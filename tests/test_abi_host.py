@@ -218,3 +218,27 @@ def test_decode_rejects_bad_arguments():
     with pytest.raises(cosa.CosaError) as e:
         cosa.cosa_osk_decode(wide.c, ptr, ptr, ptr, ptr, ptr, 4, 64, 0.0, 1, ptr, ptr, ptr, None, ptr, 1 << 30, None)
     assert e.value.status == -2
+
+
+def test_rank_and_second_order_reject_bad_arguments():
+    _lib_or_skip()
+    p = _problem((2048,))
+    ptr = FakeDev(1, 16).data_ptr()
+    ws = cosa.cosa_cobs_workspace_size(p.c, 16)
+    assert ws == 128 * 32 * 128 * 2  # pooled queries, bf16
+    assert cosa.cosa_cobs_workspace_size(p.c, 3) == 0
+    for args, status in [((3, 0.1, ptr, ptr, ptr, ptr, 26), -1), ((16, 0.0, ptr, ptr, ptr, ptr, 26), -1),
+                         ((16, 0.1, None, ptr, ptr, ptr, 26), -1), ((16, 0.1, ptr, ptr, ptr, ptr, 1), -1)]:
+        with pytest.raises(cosa.CosaError) as e:
+            cosa.cosa_kap_rank(p.c, *args, None, None)
+        assert e.value.status == status, args
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_cobs_scores(p.c, ptr, ptr, 16, ptr, ptr, 16, None)  # workspace too small
+    assert e.value.status == -3
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_cobs_scores(p.c, ptr, ptr, 16, None, ptr, 1 << 30, None)
+    assert e.value.status == -1
+    f32 = _problem((1024,), h_q=1, h_kv=1, d=64, B=64, dtype=cosa.COSA_F32)
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_cobs_scores(f32.c, ptr, ptr, 8, ptr, ptr, 1 << 30, None)
+    assert e.value.status == -2
