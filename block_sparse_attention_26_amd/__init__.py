@@ -9,12 +9,13 @@ Low-level functions carry the C names (``cosa_kap_order``,
 ``cosa_osk_attention``, ``cosa_dense_attention``, ``cosa_mask_from_order``,
 ``cosa_order_from_mask``, ``cosa_osk_attention_masked``, ``cosa_block_mass``,
 ``cosa_union_order``, ``cosa_osk_decode``, ``cosa_osk_decode_workspace_size``,
-``cosa_kap_rank``, ``cosa_cobs_scores``, ``cosa_cobs_workspace_size``,
+``cosa_kap_rank``, ``cosa_cobs_scores``, ``cosa_cobs_workspace_size``, ``cosa_kap_pool_keys``,
+``cosa_kap_order_pooled``,
 ``cosa_validate``,
 ``cosa_dims``, ``cosa_kap_workspace_size``) and take integer device pointers.
 The ``Problem`` class and the ``kap_order`` / ``osk_attention`` /
 ``dense_attention`` / ``mask_from_order`` / ``order_from_mask`` /
-``osk_attention_masked`` / ``block_mass`` / ``union_order`` / ``osk_decode`` / ``kap_rank`` / ``cobs_scores`` helpers accept torch tensors that already live on the
+``osk_attention_masked`` / ``block_mass`` / ``union_order`` / ``osk_decode`` / ``kap_rank`` / ``cobs_scores`` / ``pool_keys`` helpers accept torch tensors that already live on the
 GPU and allocate the outputs with torch.
 """
 from __future__ import annotations
@@ -31,8 +32,8 @@ __all__ = [
     "cosa_last_error", "cosa_version", "cosa_mask_from_order", "cosa_order_from_mask",
     "cosa_osk_attention_masked", "cosa_block_mass", "cosa_union_order",
     "cosa_osk_decode", "cosa_osk_decode_workspace_size", "cosa_kap_rank", "cosa_cobs_scores",
-    "cosa_cobs_workspace_size",
-    "kap_order", "osk_attention", "dense_attention", "mask_from_order", "order_from_mask",
+    "cosa_cobs_workspace_size", "cosa_kap_pool_keys", "cosa_kap_order_pooled",
+    "kap_order", "pool_keys", "osk_attention", "dense_attention", "mask_from_order", "order_from_mask",
     "osk_attention_masked", "mask_words_for", "block_mass", "union_order", "osk_decode", "kap_rank",
     "cobs_scores",
     "COSA_F32", "COSA_BF16", "EXPORTED_SYMBOLS",
@@ -49,7 +50,7 @@ EXPORTED_SYMBOLS = (
     "cosa_last_error", "cosa_version", "cosa_mask_from_order", "cosa_order_from_mask",
     "cosa_osk_attention_masked", "cosa_block_mass", "cosa_union_order",
     "cosa_osk_decode", "cosa_osk_decode_workspace_size", "cosa_kap_rank", "cosa_cobs_scores",
-    "cosa_cobs_workspace_size",
+    "cosa_cobs_workspace_size", "cosa_kap_pool_keys", "cosa_kap_order_pooled",
 )
 
 
@@ -108,6 +109,8 @@ def load():
         "cosa_union_order": (i32, [P, vp, vp, i32, vp, vp, i32, vp]),
         "cosa_osk_decode_workspace_size": (sz, [P, i32]),
         "cosa_kap_rank": (i32, [P, i32, f64, vp, vp, vp, vp, i32, vp, vp]),
+        "cosa_kap_pool_keys": (i32, [P, vp, i32, vp, i32, vp]),
+        "cosa_kap_order_pooled": (i32, [P, vp, vp, i32, f64, vp, vp, vp, i32, vp, vp, vp, sz, vp]),
         "cosa_cobs_workspace_size": (sz, [P, i32]),
         "cosa_cobs_scores": (i32, [P, vp, vp, i32, vp, vp, sz, vp]),
         "cosa_osk_decode": (i32, [P, vp, vp, vp, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, vp, sz, vp]),
@@ -190,6 +193,18 @@ def cosa_osk_attention_masked(problem, q, k_pages, v_pages, mask, mask_words, gr
     _check(load().cosa_osk_attention_masked(ctypes.byref(problem), q, k_pages, v_pages, mask,
                                             int(mask_words), int(group), float(skip_threshold), o,
                                             visited, skipped, lse, stream))
+
+
+def cosa_kap_pool_keys(problem, k_pages, pool, pooled_keys, last_block_only, stream) -> None:
+    _check(load().cosa_kap_pool_keys(ctypes.byref(problem), k_pages, int(pool), pooled_keys,
+                                     1 if last_block_only else 0, stream))
+
+
+def cosa_kap_order_pooled(problem, q, pooled_keys, pool, budget, order, hrm, count, kmax,
+                          proxy_scores, block_scores, workspace, workspace_bytes, stream) -> None:
+    _check(load().cosa_kap_order_pooled(ctypes.byref(problem), q, pooled_keys, int(pool), float(budget),
+                                        order, hrm, count, int(kmax), proxy_scores, block_scores,
+                                        workspace, int(workspace_bytes), stream))
 
 
 def cosa_kap_rank(problem, pool, budget, scores, order, hrm, count, kmax, block_scores, stream) -> None:
@@ -283,10 +298,22 @@ class Problem:
         return cosa_validate(self.c)
 
 
+def pool_keys(problem: Problem, k_pages, pool: int, *, out=None, last_block_only: bool = False, stream=None):
+    """Pooled keys [num_pages, h_kv, B/p, d] (into ``out`` when given)."""
+    import torch
+    c = problem.c
+    if out is None:
+        out = torch.zeros((c.num_pages, c.h_kv, c.block // pool, c.head_dim), dtype=k_pages.dtype,
+                          device=k_pages.device)
+    cosa_kap_pool_keys(c, k_pages.data_ptr(), pool, out.data_ptr(), last_block_only, _stream(stream))
+    return out
+
+
 def kap_order(problem: Problem, q, k_pages, pool: int, budget: float, *, kmax=None,
               export_scores: bool = False, export_block_scores: bool = False,
-              workspace=None, stream=None):
-    """Run the proxy; returns dict(order, hrm, count, kmax[, P][, s])."""
+              workspace=None, pooled_keys=None, stream=None):
+    """Run the proxy; returns dict(order, hrm, count, kmax[, P][, s]). With
+    ``pooled_keys`` (from ``pool_keys``) the keys are not pooled again."""
     import torch
     dev = q.device
     d = problem.dims(pool, budget)
@@ -301,9 +328,14 @@ def kap_order(problem: Problem, q, k_pages, pool: int, budget: float, *, kmax=No
     ws_bytes = cosa_kap_workspace_size(problem.c, pool, P is None)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    cosa_kap_order(problem.c, q.data_ptr(), k_pages.data_ptr(), pool, budget, order.data_ptr(),
-                   hrm.data_ptr(), count.data_ptr(), kmax, _ptr(P), _ptr(s), workspace.data_ptr(),
-                   workspace.numel(), _stream(stream))
+    if pooled_keys is None:
+        cosa_kap_order(problem.c, q.data_ptr(), k_pages.data_ptr(), pool, budget, order.data_ptr(),
+                       hrm.data_ptr(), count.data_ptr(), kmax, _ptr(P), _ptr(s), workspace.data_ptr(),
+                       workspace.numel(), _stream(stream))
+    else:
+        cosa_kap_order_pooled(problem.c, q.data_ptr(), pooled_keys.data_ptr(), pool, budget, order.data_ptr(),
+                              hrm.data_ptr(), count.data_ptr(), kmax, _ptr(P), _ptr(s), workspace.data_ptr(),
+                              workspace.numel(), _stream(stream))
     out = {"order": order, "hrm": hrm, "count": count, "kmax": kmax, "workspace": workspace}
     if P is not None:
         out["P"] = P

@@ -83,8 +83,8 @@ def run(args) -> list:
     import numpy as np
     import torch
 
-    import block_sparse_attention_26_amd as cosa
     sys.path.insert(0, ROOT)
+    import block_sparse_attention_26_amd as cosa
     import synthetic
 
     if not torch.cuda.is_available():

@@ -269,18 +269,19 @@ size_t cosa_kap_workspace_size(const cosa_problem* problem, int32_t pool, int32_
   return kap_ws_size(problem, pool, with_scores != 0);
 }
 
-cosa_status cosa_kap_order(const cosa_problem* problem, const void* q, const void* k_pages,
-                           int32_t pool, double budget, int32_t* order, uint8_t* hrm,
-                           int32_t* count, int32_t kmax, float* proxy_scores,
-                           float* block_scores, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+// the proxy with its own key pooling (k_pages) or over caller-pooled keys
+static cosa_status run_kap(const cosa_problem* problem, const void* q, const void* k_pages, const void* pooled_keys,
+                           int32_t pool, double budget, int32_t* order, uint8_t* hrm, int32_t* count, int32_t kmax,
+                    float* proxy_scores, float* block_scores, void* workspace, size_t workspace_bytes,
+                    void* stream) {
   cosa_status st = validate(problem);
   if (st != COSA_OK) return st;
   if ((st = check_pool(problem, pool)) != COSA_OK) return st;
   if (!(budget > 0.0 && budget <= 1.0))
     return fail(COSA_ERR_INVALID_ARG, "budget must lie in (0, 1] (got %g)", budget);
-  if (!q || !k_pages || !order || !hrm || !count)
-    return fail(COSA_ERR_INVALID_ARG, "q, k_pages, order, hrm and count must be non-NULL");
+  if (!q || !(k_pages || pooled_keys) || !order || !hrm || !count)
+    return fail(COSA_ERR_INVALID_ARG, pooled_keys ? "q, pooled_keys, order, hrm and count must be non-NULL"
+                                                  : "q, k_pages, order, hrm and count must be non-NULL");
   cosa_dims_t d;
   compute_dims(problem, pool, budget, &d);
   if (kmax < d.kmax)
@@ -306,13 +307,15 @@ cosa_status cosa_kap_order(const cosa_problem* problem, const void* q, const voi
   a.k = k_pages;
   a.q_pool = ws;
   ws += align256((size_t)problem->batch * d.max_nr * problem->h_q * problem->head_dim * es);
-  a.k_pool = ws;
+  a.k_pool = pooled_keys ? const_cast<void*>(pooled_keys) : (void*)ws;  // read only when given
+  a.keys_pooled = pooled_keys ? 1 : 0;
   ws += align256((size_t)problem->num_pages * problem->h_kv * (problem->block / pool) *
                  problem->head_dim * es);
   // the score pass reduces rows of P to their maxima when blocks hold 4..32
-  // pooled keys; otherwise the rank pass does
+  // pooled keys (not in its decode shape); otherwise the rank pass does
   const int per = problem->block / pool;
-  a.row_max = (per >= 4 && per <= 32) ? (float*)ws : nullptr;
+  const bool decode_scores = cosa::kap_decode_scores(d.max_nr, problem->h_q / problem->h_kv, per, problem->dtype);
+  a.row_max = (per >= 4 && per <= 32 && !decode_scores) ? (float*)ws : nullptr;
   ws += align256((size_t)problem->batch * problem->h_q * d.max_nr * sizeof(float));
   a.scores = own_scores ? (float*)ws : proxy_scores;
   a.fill_scores = own_scores ? 0 : 1;
@@ -328,6 +331,45 @@ cosa_status cosa_kap_order(const cosa_problem* problem, const void* q, const voi
   return hip_result(cosa::launch_kap(a, problem->dtype, problem->head_dim, problem->block,
                                      (hipStream_t)stream),
                     "KAP launch");
+}
+
+cosa_status cosa_kap_order(const cosa_problem* problem, const void* q, const void* k_pages,
+                           int32_t pool, double budget, int32_t* order, uint8_t* hrm,
+                           int32_t* count, int32_t kmax, float* proxy_scores,
+                           float* block_scores, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return run_kap(problem, q, k_pages, nullptr, pool, budget, order, hrm, count, kmax, proxy_scores,
+                 block_scores, workspace, workspace_bytes, stream);
+}
+
+cosa_status cosa_kap_order_pooled(const cosa_problem* problem, const void* q, const void* pooled_keys,
+                                  int32_t pool, double budget, int32_t* order, uint8_t* hrm,
+                                  int32_t* count, int32_t kmax, float* proxy_scores,
+                                  float* block_scores, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (!pooled_keys) return fail(COSA_ERR_INVALID_ARG, "pooled_keys must be non-NULL");
+  return run_kap(problem, q, nullptr, pooled_keys, pool, budget, order, hrm, count, kmax, proxy_scores,
+                 block_scores, workspace, workspace_bytes, stream);
+}
+
+cosa_status cosa_kap_pool_keys(const cosa_problem* problem, const void* k_pages, int32_t pool,
+                               void* pooled_keys, int32_t last_block_only, void* stream) {
+  cosa_status st = validate(problem);
+  if (st != COSA_OK) return st;
+  if ((st = check_pool(problem, pool)) != COSA_OK) return st;
+  if (!k_pages || !pooled_keys) return fail(COSA_ERR_INVALID_ARG, "k_pages and pooled_keys must be non-NULL");
+  cosa_dims_t d;
+  compute_dims(problem, pool, 0.0, &d);
+  if (d.max_nk == 0) return ok();
+  cosa::KapArgs a{};
+  a.seq = seq_args(problem, d);
+  a.k = k_pages;
+  a.k_pool = pooled_keys;
+  a.pool = pool;
+  a.pool_last_only = last_block_only ? 1 : 0;
+  return hip_result(cosa::launch_kap_pool_k(a, problem->dtype, problem->head_dim, problem->block,
+                                            (hipStream_t)stream),
+                    "key pooling launch");
 }
 
 cosa_status cosa_osk_attention(const cosa_problem* problem, const void* q, const void* k_pages,

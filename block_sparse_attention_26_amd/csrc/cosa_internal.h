@@ -65,7 +65,16 @@ struct KapArgs {
   int32_t kmax;
   double budget;
   float scale;
+  int32_t keys_pooled;     // k_pool already holds the pooled keys: skip key pooling
+  int32_t pool_last_only;  // key pooling: only the last KV block of each sequence
 };
+
+// The proxy scores a problem with one pooled query row per sequence (a decode
+// step) with the group's query heads as MFMA columns; that pass leaves the
+// row maxima to the rank pass.
+inline bool kap_decode_scores(int max_nr, int group, int per, int dtype) {
+  return max_nr == 1 && group <= 32 && per >= 4 && per <= 32 && dtype == 1;
+}
 
 // Mask <-> list conversions (one wave per row of batch * h_kv * max_nq).
 struct MaskArgs {
@@ -127,6 +136,7 @@ hipError_t launch_kap(const KapArgs& a, int dtype, int head_dim, int block, hipS
 // single stages: query pooling (bf16) and the rank/sort pass over given scores
 hipError_t launch_kap_pool_q(const KapArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_kap_rank(const KapArgs& a, int block, hipStream_t stream);
+hipError_t launch_kap_pool_k(const KapArgs& a, int dtype, int head_dim, int block, hipStream_t stream);
 hipError_t launch_cobs_scores(const KapArgs& a, int head_dim, int block, hipStream_t stream);
 hipError_t launch_mask_from_order(const MaskArgs& a, hipStream_t stream);
 hipError_t launch_order_from_mask(const MaskArgs& a, hipStream_t stream);

@@ -101,9 +101,11 @@ __global__ __launch_bounds__(kThreads) void kap_pool_q(KapArgs a) {
 template <bool BF16, int D, int BLK>
 __global__ __launch_bounds__(kThreads) void kap_pool_k(KapArgs a) {
   const SeqArgs& sq = a.seq;
-  const int b = blockIdx.x / sq.max_nk, kb = blockIdx.x % sq.max_nk;
+  // all blocks, or (decode) only the last block of each sequence
+  const int b = a.pool_last_only ? blockIdx.x : blockIdx.x / sq.max_nk;
   const int Lk = sq.seqlens_k[b];
-  if (kb * BLK >= Lk) return;
+  const int kb = a.pool_last_only ? (Lk - 1) / BLK : blockIdx.x % sq.max_nk;
+  if (Lk <= 0 || kb * BLK >= Lk) return;
   const int page = sq.block_table[(int64_t)b * sq.max_blocks_k + kb];
   if ((unsigned)page >= (unsigned)sq.num_pages) return;
   const int nvalid = min(BLK, Lk - kb * BLK);
@@ -426,6 +428,128 @@ __device__ float exp32(float x) {
 // One workgroup per (sequence, KV group, query block), longest rows first.
 constexpr int kMaxRankRows = 4096;  // G * (B/p) pooled rows per list
 
+// ---- proxy scores for decode problems (one pooled query row per sequence) --
+// The G query heads of a KV group are the MFMA columns (Kpool . Qpool^T with
+// G of 32 columns used), so one workgroup scores a chunk of kDecodeKeys
+// pooled keys for the whole group; blocks of 4..32 pooled keys are reduced in
+// registers as in kap_score. Row maxima are left to the rank pass.
+constexpr int kDecodeKeys = 1024;
+
+template <int D, int BLK>
+__global__ __launch_bounds__(kThreads) void kap_score_decode(KapArgs a) {
+  const SeqArgs& sq = a.seq;
+  const int G = sq.group;
+  const int p = a.pool;
+  const int per = BLK / p;
+  const int nchunk = (sq.max_nk * per + kDecodeKeys - 1) / kDecodeKeys;
+  const int64_t bid = blockIdx.x;
+  const int chunk = (int)(bid % nchunk);
+  const int g = (int)(bid / nchunk % sq.h_kv);
+  const int b = (int)(bid / nchunk / sq.h_kv);
+  const int q0 = sq.cu_seqlens_q[b];
+  const int Lq = sq.cu_seqlens_q[b + 1] - q0;
+  const int Lk = sq.seqlens_k[b];
+  const int off = Lk - Lq;
+  const int Rk = (Lk + p - 1) / p;
+  const int nk = (Lk + BLK - 1) / BLK;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hl = lane >> 5;
+  const bool col_ok = l32 < G && Lq > 0;  // column l32 is query head g*G + l32
+  const int h = g * G + (l32 < G ? l32 : 0);
+  const int jmax = Lq > 0 ? (off + min(p - 1, Lq - 1)) / p : -1;  // last pooled key row 0 sees
+  const int kb0 = chunk * (kDecodeKeys / per);
+  const int kb1 = min(kb0 + kDecodeKeys / per, sq.max_nk);
+  const int kb_end = Lq > 0 ? min(min(jmax / per + 1, nk), kb1) : kb0;  // computed: [kb0, kb_end)
+  if (a.fill_scores && lane < 32 && l32 < G)
+    for (int kb = max(kb_end, kb0) + w * 1; kb < kb1; kb += kThreads / 64)  // blocks no key of which is seen
+      a.scores[(((int64_t)b * sq.h_q + g * G + l32) * a.max_nr) * sq.max_nk + kb] = kNegInf;
+  if (kb_end <= kb0) return;
+
+  constexpr int QREGS = D / 16;
+  bf16x8 qf[QREGS];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q_pool + (((size_t)b * a.max_nr) * sq.h_q + h) * D + hl * 8;
+#pragma unroll
+    for (int ks = 0; ks < QREGS; ++ks) {
+      const uint4 x = col_ok ? *(const uint4*)(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+      qf[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  const int jend = kb_end * per;
+  auto key_off = [&](int j0) -> int64_t {
+    const int jk = j0 + w * 32 + l32;
+    if (!(jk < Rk && jk < jend)) return -1;
+    const int page = sq.block_table[(int64_t)b * sq.max_blocks_k + jk / per];
+    return (int64_t)((((size_t)page * sq.h_kv + g) * per) + jk % per) * D;
+  };
+  uint4 kc[QREGS], kn[QREGS];
+  int64_t koff = key_off(kb0 * per);
+  {
+    const uint16_t* kp = (const uint16_t*)a.k_pool + (koff < 0 ? 0 : koff) + hl * 8;
+#pragma unroll
+    for (int ks = 0; ks < QREGS; ++ks) kc[ks] = koff >= 0 ? *(const uint4*)(kp + ks * 16) : make_uint4(0, 0, 0, 0);
+  }
+  float* P = a.scores + (((int64_t)b * sq.h_q + h) * a.max_nr) * sq.max_nk;
+  for (int j0 = kb0 * per; j0 < jend; j0 += kScoreKeys) {
+    const int64_t koff_n = j0 + kScoreKeys < jend ? key_off(j0 + kScoreKeys) : -1;
+    {
+      const uint16_t* kp = (const uint16_t*)a.k_pool + (koff_n < 0 ? 0 : koff_n) + hl * 8;
+#pragma unroll
+      for (int ks = 0; ks < QREGS; ++ks)
+        kn[ks] = koff_n >= 0 ? *(const uint4*)(kp + ks * 16) : make_uint4(0, 0, 0, 0);
+    }
+    f32x16 sc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < QREGS; ++ks)
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kc[ks]), qf[ks], sc, 0, 0, 0);
+    // element v: pooled key j0 + w*32 + 8*(v/4) + 4*hl + v%4 (raw dot; scaled after the max)
+    float x[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int j = j0 + w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3);
+      x[v] = (j <= jmax && j < Rk) ? sc[v] : kNegInf;
+    }
+    float g4[4], o4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) g4[q] = fmaxf(fmaxf(x[4 * q], x[4 * q + 1]), fmaxf(x[4 * q + 2], x[4 * q + 3]));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(g4[q]), __float_as_uint(g4[q]), false, false);
+      o4[q] = __uint_as_float(hl ? sw[0] : sw[1]);
+    }
+    if (hl == 0 && col_ok) {
+      const int kbase = (j0 + w * 32) / per;
+      float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      int nb;
+      if (per == 4) {
+        nb = 8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          m[2 * q] = g4[q];
+          m[2 * q + 1] = o4[q];
+        }
+      } else if (per == 8) {
+        nb = 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) m[q] = fmaxf(g4[q], o4[q]);
+      } else if (per == 16) {
+        nb = 2;
+        m[0] = fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1]));
+        m[1] = fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3]));
+      } else {
+        nb = 1;
+        m[0] = fmaxf(fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1])), fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3])));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < nb && kbase + i < kb_end) P[kbase + i] = m[i] * a.scale;
+    }
+#pragma unroll
+    for (int ks = 0; ks < QREGS; ++ks) kc[ks] = kn[ks];
+  }
+}
+
 template <int BLK>
 __global__ __launch_bounds__(kThreads) void kap_rank_sort(KapArgs a) {
   __shared__ unsigned long long keys[kMaxSortBlocks];
@@ -574,11 +698,18 @@ hipError_t launch_all(const KapArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((kap_pool_q<BF16, D>), dim3((unsigned)g1), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t g2 = (int64_t)sq.batch * sq.max_nk;
-  hipLaunchKernelGGL((kap_pool_k<BF16, D, BLK>), dim3((unsigned)g2), dim3(kThreads), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!a.keys_pooled) {
+    const int64_t g2 = (int64_t)sq.batch * sq.max_nk;
+    hipLaunchKernelGGL((kap_pool_k<BF16, D, BLK>), dim3((unsigned)g2), dim3(kThreads), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int per = BLK / a.pool;
-  if (per >= 4 && per <= 32) {  // block maxima in registers: two row tiles share each K load
+  if (BF16 && kap_decode_scores(a.max_nr, sq.group, per, 1)) {  // one pooled row: heads as columns
+    const int64_t nchunk = ((int64_t)sq.max_nk * per + kDecodeKeys - 1) / kDecodeKeys;
+    const int64_t g3 = nchunk * sq.h_kv * sq.batch;
+    if constexpr (BF16)
+      hipLaunchKernelGGL((kap_score_decode<D, BLK>), dim3((unsigned)g3), dim3(kThreads), 0, stream, a);
+  } else if (per >= 4 && per <= 32) {  // block maxima in registers: two row tiles share each K load
     const int64_t ntile = (a.max_nr + 2 * kScoreRows - 1) / (2 * kScoreRows);
     const int64_t g3 = ntile * sq.batch * sq.h_q;
     hipLaunchKernelGGL((kap_score<BF16, D, BLK, 2>), dim3((unsigned)g3), dim3(kThreads), 0, stream, a);
@@ -604,6 +735,25 @@ hipError_t launch_kap_pool_q(const KapArgs& a, int dtype, int head_dim, hipStrea
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_kap_pool_k(const KapArgs& a, int dtype, int head_dim, int block, hipStream_t stream) {
+  const int64_t g2 = a.pool_last_only ? (int64_t)a.seq.batch : (int64_t)a.seq.batch * a.seq.max_nk;
+#define COSA_POOLK_CASE(BF, DD, BB)                                                                   \
+  if ((dtype == 1) == BF && head_dim == DD && block == BB) {                                           \
+    hipLaunchKernelGGL((kap_pool_k<BF, DD, BB>), dim3((unsigned)g2), dim3(kThreads), 0, stream, a); \
+    return hipGetLastError();                                                                          \
+  }
+  COSA_POOLK_CASE(true, 128, 128)
+  COSA_POOLK_CASE(true, 128, 64)
+  COSA_POOLK_CASE(true, 64, 128)
+  COSA_POOLK_CASE(true, 64, 64)
+  COSA_POOLK_CASE(false, 128, 128)
+  COSA_POOLK_CASE(false, 128, 64)
+  COSA_POOLK_CASE(false, 64, 128)
+  COSA_POOLK_CASE(false, 64, 64)
+#undef COSA_POOLK_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_kap_rank(const KapArgs& a, int block, hipStream_t stream) {

@@ -3,10 +3,11 @@ long KV cache, through the library's C ABI.
 
 For a batch of sequences (default 8 x 131072 cached tokens, 32 query / 8 KV
 heads, head_dim 128, bf16, block 128, pool 16, budget 10%, tau e^-16) it times
-the proxy (cosa_kap_order on the decode problem, which re-pools the whole
-cache every call), the split decode walk (cosa_osk_decode) for several
-segment counts, and the same walk over every causal block with skipping off
-(dense decode). The walk is bandwidth-bound: its roofline is the K and V
+the proxy two ways - cosa_kap_order re-pooling the whole cache, and the
+decode-loop form that keeps pooled keys (cosa_kap_pool_keys on each
+sequence's last block, then cosa_kap_order_pooled) - the split decode walk
+(cosa_osk_decode) for several segment counts, and the same walk over every
+causal block with skipping off (dense decode). The walk is bandwidth-bound: its roofline is the K and V
 bytes of the walked pages over the 8 TB/s HBM peak.
 
     python -m block_sparse_attention_26_amd.decode_bench [--batch 8] [--context 131072]
@@ -57,8 +58,8 @@ def main(argv=None):
 
     import torch
 
-    import block_sparse_attention_26_amd as cosa
     sys.path.insert(0, ROOT)
+    import block_sparse_attention_26_amd as cosa
     import synthetic
 
     if not torch.cuda.is_available():
@@ -75,6 +76,15 @@ def main(argv=None):
     d = pr.dims(case.pool, case.budget)
     tile_bytes = case.block * case.head_dim * 2  # one K or V slab of a page and KV head
     ka, kap_ms = _timed(lambda: cosa.kap_order(pr, q, k, case.pool, case.budget), args.reps, stream)
+    pooled = cosa.pool_keys(pr, k, case.pool)  # the decode loop's standing pooled keys
+
+    def proxy_step():
+        cosa.pool_keys(pr, k, case.pool, out=pooled, last_block_only=True)
+        return cosa.kap_order(pr, q, k, case.pool, case.budget, pooled_keys=pooled)
+
+    kp, kap_pooled_ms = _timed(proxy_step, args.reps, stream)
+    for name in ("order", "hrm", "count"):
+        assert torch.equal(kp[name], ka[name]), name  # same lists either way
     full = cosa.order_from_mask(pr, None, d.max_nk, device=dev)
     dn, dense_ms = _timed(lambda: cosa.osk_decode(pr, q, k, v, full["order"], full["count"], 0.0, 16),
                           args.reps, stream)
@@ -88,7 +98,8 @@ def main(argv=None):
     rows = [{"mode": "dense-decode", "walk_ms": dense_ms, "splits": 16,
              "hbm_gbs": causal * 2 * tile_bytes / (dense_ms * 1e-3) / 1e9}]
     rows[0]["hbm_frac"] = rows[0]["hbm_gbs"] / HBM_PEAK_GBS
-    _log(f"proxy {kap_ms:.3f} ms; dense decode {dense_ms:.3f} ms ({rows[0]['hbm_gbs']:.0f} GB/s)")
+    _log(f"proxy {kap_ms:.3f} ms re-pooling the cache, {kap_pooled_ms:.3f} ms with kept pooled keys; "
+         f"dense decode {dense_ms:.3f} ms ({rows[0]['hbm_gbs']:.0f} GB/s)")
     for S in [int(x) for x in args.splits.split(",")]:
         res, ms = _timed(lambda: cosa.osk_decode(pr, q, k, v, ka["order"], ka["count"], case.tau, S),
                          args.reps, stream)
@@ -96,6 +107,7 @@ def main(argv=None):
         skipped = int(res["skipped"].sum())
         err = res["O"].float() - O_ref
         row = {"mode": "cosa-decode", "splits": S, "walk_ms": ms, "proxy_ms": kap_ms,
+               "proxy_pooled_ms": kap_pooled_ms, "step_ms": kap_pooled_ms + ms,
                "hbm_gbs": listed * 2 * tile_bytes / (ms * 1e-3) / 1e9,
                "visited": visited, "skipped": skipped,
                "rel_l2_vs_dense": float(err.norm() / O_ref.norm())}

@@ -193,6 +193,24 @@ cosa_status cosa_osk_attention(const cosa_problem* problem, const void* q, const
 cosa_status cosa_dense_attention(const cosa_problem* problem, const void* q, const void* k_pages,
                                  const void* v_pages, void* o, float* lse, void* stream);
 
+/* ---- Pooled keys kept across calls (decode loops) ------------------------------
+ * cosa_kap_pool_keys writes the proxy's pooled keys (mean over p consecutive
+ * keys, as inside cosa_kap_order) into a caller-owned buffer
+ * pooled_keys [num_pages, h_kv, B/p, head_dim] in the problem's dtype, laid
+ * out like the pages so the block table applies. last_block_only = 0 pools
+ * every KV block of every sequence; 1 pools only the last block of each
+ * sequence, the one a decode step appends to, so a loop that keeps the
+ * buffer pools one page per step instead of the whole cache.
+ * cosa_kap_order_pooled is cosa_kap_order reading those pooled keys instead
+ * of pooling k_pages (same outputs, workspace and limits). */
+cosa_status cosa_kap_pool_keys(const cosa_problem* problem, const void* k_pages, int32_t pool,
+                               void* pooled_keys, int32_t last_block_only, void* stream);
+cosa_status cosa_kap_order_pooled(const cosa_problem* problem, const void* q, const void* pooled_keys,
+                                  int32_t pool, double budget, int32_t* order, uint8_t* hrm,
+                                  int32_t* count, int32_t kmax, float* proxy_scores,
+                                  float* block_scores, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
 /* ---- Ranking from given scores; second-order scores ---------------------------
  * cosa_kap_rank runs the proxy's MaxNorm, HRM flags, sort and budget (as in
  * cosa_kap_order, bit for bit) on a caller's score tensor

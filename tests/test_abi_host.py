@@ -242,3 +242,21 @@ def test_rank_and_second_order_reject_bad_arguments():
     with pytest.raises(cosa.CosaError) as e:
         cosa.cosa_cobs_scores(f32.c, ptr, ptr, 8, ptr, ptr, 1 << 30, None)
     assert e.value.status == -2
+
+
+def test_pooled_key_entry_points_reject_bad_arguments():
+    _lib_or_skip()
+    p = _problem((2048,))
+    ptr = FakeDev(1, 16).data_ptr()
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_kap_pool_keys(p.c, ptr, 3, ptr, 0, None)
+    assert e.value.status == -1
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_kap_pool_keys(p.c, None, 16, ptr, 0, None)
+    assert e.value.status == -1
+    with pytest.raises(cosa.CosaError) as e:
+        cosa.cosa_kap_order_pooled(p.c, ptr, None, 16, 0.1, ptr, ptr, ptr, 26, None, None, ptr, 1 << 40, None)
+    assert e.value.status == -1
+    with pytest.raises(cosa.CosaError) as e:  # workspace too small
+        cosa.cosa_kap_order_pooled(p.c, ptr, ptr, 16, 0.1, ptr, ptr, ptr, 26, None, None, ptr, 16, None)
+    assert e.value.status == -3

@@ -136,3 +136,55 @@ def test_decode_empty_and_corrupt_lists(run):
     keep = ~touched
     assert np.array_equal(O[keep].view(np.uint32), O0[keep].view(np.uint32))
     assert np.array_equal(lse.T[keep].view(np.uint32), lse0.T[keep].view(np.uint32))
+
+
+def test_decode_proxy_scores_tolerance(run):
+    """Decode problems take the heads-as-columns score pass; its P stays within
+    the max-pooled scores' tolerance of the fp64 oracle."""
+    case, dev = run["case"], run["dev"]
+    say(run["name"], "decode proxy scores")
+    k = cosa.kap_order(dev.problem, dev.q, dev.k, case.pool, case.budget, export_scores=True)
+    torch.cuda.synchronize()
+    P = k["P"].cpu().numpy()
+    P64 = oc.kap_case(case, precision="fp64")["P"]
+    fin = np.isfinite(P64)
+    assert np.array_equal(np.isfinite(P), fin)
+    assert np.all(P[~fin] == -np.inf)
+    assert np.abs(P[fin] - P64[fin]).max() <= 1e-2 * np.abs(P64[fin]).max()
+
+
+def _shorter(problem_case, dev, drop):
+    """The same batch with `drop` fewer cached tokens per non-empty sequence."""
+    case = problem_case
+    lk = [max(int(x) - drop, q) for x, q in zip(case.seqlens_k.tolist(), case.seqlens_q)]
+    cu = case.cu_seqlens_q.tolist()
+    return cosa.Problem(h_q=case.h_q, h_kv=case.h_kv, head_dim=case.head_dim, block=case.block,
+                        dtype=cosa.COSA_BF16, softmax_scale=case.scale, num_pages=int(case.k_pages.shape[0]),
+                        cu_seqlens_q=case.cu_seqlens_q.cuda(), seqlens_k=torch.tensor(lk, dtype=torch.int32).cuda(),
+                        block_table=case.block_table.cuda(), host_cu_seqlens_q=cu, host_seqlens_k=lk)
+
+
+def test_pooled_keys_reused_and_updated(run):
+    """Pooled keys kept across calls give the proxy's own lists and scores bit
+    for bit, and re-pooling only each sequence's last block after a token is
+    appended reproduces a full re-pooling."""
+    case, dev = run["case"], run["dev"]
+    say(run["name"], "pooled keys")
+    pooled = cosa.pool_keys(dev.problem, dev.k, case.pool)
+    a = cosa.kap_order(dev.problem, dev.q, dev.k, case.pool, case.budget, export_scores=True)
+    b = cosa.kap_order(dev.problem, dev.q, dev.k, case.pool, case.budget, export_scores=True, pooled_keys=pooled)
+    torch.cuda.synchronize()
+    for name in ("order", "hrm", "count"):
+        assert torch.equal(a[name], b[name]), name
+    assert torch.equal(a["P"].view(torch.int32), b["P"].view(torch.int32))
+    for drop in (1, 37):
+        prev = _shorter(case, dev, drop)
+        buf = cosa.pool_keys(prev, dev.k, case.pool)
+        if drop == 1:  # one appended token: only the last block changes
+            cosa.pool_keys(dev.problem, dev.k, case.pool, out=buf, last_block_only=True)
+            torch.cuda.synchronize()
+            assert torch.equal(buf.view(torch.int16), pooled.view(torch.int16))
+        else:  # several tokens may span a block boundary: a full pass is needed, and matches
+            cosa.pool_keys(dev.problem, dev.k, case.pool, out=buf)
+            torch.cuda.synchronize()
+            assert torch.equal(buf.view(torch.int16), pooled.view(torch.int16))
