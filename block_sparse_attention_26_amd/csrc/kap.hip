@@ -550,6 +550,79 @@ __global__ __launch_bounds__(kThreads) void kap_score_decode(KapArgs a) {
   }
 }
 
+// ---- descending bitonic sort of 256*E unique 64-bit keys -------------------
+// Thread t holds entries t*E .. t*E+E-1 in registers. Stages whose partner is
+// in the same thread swap registers, stages within a wave exchange through
+// cross-lane shuffles, and only stages across waves go through LDS (`lds`
+// holds 256*E keys). The network's result is the unique descending order.
+__device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, int m) {
+  const int lo = __shfl_xor((int)(uint32_t)v, m, 64);
+  const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+template <int E>
+__device__ __forceinline__ void bitonic_desc(unsigned long long (&x)[E], unsigned long long* lds, int tid) {
+  constexpr int N = kThreads * E;
+  const int lane = tid & 63;
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j >= E; j >>= 1) {
+      if (j < 64 * E) {  // partner: the same register of lane ^ (j / E)
+        const int m = j / E;
+        const bool lower = (lane & m) == 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const unsigned long long y = shfl_xor64(x[e], m);
+          const bool desc = ((tid * E + e) & k) == 0;
+          const bool take_max = lower == desc;
+          x[e] = take_max ? (x[e] > y ? x[e] : y) : (x[e] < y ? x[e] : y);
+        }
+      } else {  // partner in another wave
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) lds[tid * E + e] = x[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = tid * E + e;
+          const unsigned long long y = lds[i ^ j];
+          const bool take_max = ((i & j) == 0) == ((i & k) == 0);
+          x[e] = take_max ? (x[e] > y ? x[e] : y) : (x[e] < y ? x[e] : y);
+        }
+      }
+    }
+#pragma unroll
+    for (int jj = E / 2; jj >= 1; jj >>= 1) {  // partner in the same thread
+      if (jj <= (k >> 1)) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if ((e & jj) == 0) {
+            const int q = e | jj;
+            const bool desc = ((tid * E + e) & k) == 0;
+            const unsigned long long lo = x[e], hi = x[q];
+            const bool sw = desc ? (lo < hi) : (lo > hi);
+            x[e] = sw ? hi : lo;
+            x[q] = sw ? lo : hi;
+          }
+        }
+      }
+    }
+  }
+}
+
+// sorts keys[0 .. N) (N = 256*E) descending, leaving the result in keys
+template <int E>
+__device__ __forceinline__ void sort_keys_desc(unsigned long long* keys, int tid) {
+  unsigned long long x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = keys[tid * E + e];
+  bitonic_desc<E>(x, keys, tid);
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e) keys[tid * E + e] = x[e];
+  __syncthreads();
+}
+
 template <int BLK>
 __global__ __launch_bounds__(kThreads) void kap_rank_sort(KapArgs a) {
   __shared__ unsigned long long keys[kMaxSortBlocks];
@@ -613,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void kap_rank_sort(KapArgs a) {
   }
   __syncthreads();
 
-  int npad = 1;
+  int npad = kThreads;  // the sort network's size: a power of two, at least one key per thread
   while (npad < n) npad <<= 1;
   for (int kb = tid; kb < npad; kb += kThreads) {
     unsigned long long key = 0ull;
@@ -658,22 +731,13 @@ __global__ __launch_bounds__(kThreads) void kap_rank_sort(KapArgs a) {
     for (int kb = n + tid; kb < sq.max_nk; kb += kThreads) bs[kb] = 0.f;
   __syncthreads();
 
-  // bitonic sort, descending
-  for (int k = 2; k <= npad; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < npad; i += kThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const unsigned long long x = keys[i], y = keys[ixj];
-          const bool desc = (i & k) == 0;
-          if (desc ? (x < y) : (x > y)) {
-            keys[i] = y;
-            keys[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
+  // descending sort (padding keys are 0, below every real key)
+  switch (npad / kThreads) {
+    case 1: sort_keys_desc<1>(keys, tid); break;
+    case 2: sort_keys_desc<2>(keys, tid); break;
+    case 4: sort_keys_desc<4>(keys, tid); break;
+    case 8: sort_keys_desc<8>(keys, tid); break;
+    default: sort_keys_desc<16>(keys, tid); break;
   }
 
   int kcnt = (int)ceil(a.budget * (double)n - 1e-9);
