@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
   if constexpr (BF16) {
     const uint16_t* kp = (const uint16_t*)a.k_pool + (koff_c < 0 ? 0 : koff_c) + hl * 8;
 #pragma unroll
-    for (int ks = 0; ks < QREGS; ++ks) kc[ks] = koff_c >= 0 ? *(const uint4*)(kp + ks * 16) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < QREGS; ++ks) kc[ks] = *(const uint4*)(kp + ks * 16);  // masked when invalid
   }
   float rmx[RT];  // running row maxima over this wave's keys (RT > 1)
 #pragma unroll
@@ -238,141 +238,144 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
   int it = 0;
   // the tile's first row sees the fewest keys
   const int jmax_first = (off + min(r0 * p + p - 1, Lq - 1)) / p;
-  for (int j0 = 0; j0 < jend; j0 += kScoreKeys, ++it) {
-    const int64_t koff_n = j0 + kScoreKeys < jend ? key_off(j0 + kScoreKeys) : -1;
-    const bool edge = j0 + kScoreKeys - 1 > jmax_first || j0 + kScoreKeys > Rk;
-    if constexpr (BF16) {
-      const uint16_t* kp = (const uint16_t*)a.k_pool + (koff_n < 0 ? 0 : koff_n) + hl * 8;
+  // one 128-key step on the current fragments, loading the next step's; the
+  // loop runs two steps per trip with the fragment buffers swapped, so the
+  // prefetched fragments are never copied
+  auto step = [&](int j0, int it, uint4 (&cur)[KREGS], uint4 (&nxt)[KREGS]) {
+      const int64_t koff_n = j0 + kScoreKeys < jend ? key_off(j0 + kScoreKeys) : -1;
+      const bool edge = j0 + kScoreKeys - 1 > jmax_first || j0 + kScoreKeys > Rk;
+      if constexpr (BF16) {
+        const uint16_t* kp = (const uint16_t*)a.k_pool + (koff_n < 0 ? 0 : koff_n) + hl * 8;
 #pragma unroll
-      for (int ks = 0; ks < QREGS; ++ks) kn[ks] = koff_n >= 0 ? *(const uint4*)(kp + ks * 16) : make_uint4(0, 0, 0, 0);
-    }
-    // ---- per row tile, one 32x32 MFMA tile per wave: keys j0 + w*32 + [0,32)
-    f32x16 sc[RT];
-#pragma unroll
-    for (int u = 0; u < RT; ++u)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sc[u][v] = 0.f;
-    if constexpr (BF16) {
-#pragma unroll
-      for (int ks = 0; ks < QREGS; ++ks)
-#pragma unroll
-        for (int u = 0; u < RT; ++u)
-          sc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kc[ks]), qf16[u][ks], sc[u], 0, 0, 0);
-    } else {
-      const bool k_ok = koff_c >= 0;
-      const float* kp = (const float*)a.k_pool + (k_ok ? koff_c : 0) + hl;
-#pragma unroll
-      for (int ks = 0; ks < QREGS; ++ks) {
-        const float kv = k_ok ? kp[2 * ks] : 0.f;
-#pragma unroll
-        for (int u = 0; u < RT; ++u) sc[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv, qf32[u][ks], sc[u], 0, 0, 0);
+        for (int ks = 0; ks < QREGS; ++ks) nxt[ks] = *(const uint4*)(kp + ks * 16);  // an invalid key is masked
       }
-    }
+      // ---- per row tile, one 32x32 MFMA tile per wave: keys j0 + w*32 + [0,32)
+      f32x16 sc[RT];
 #pragma unroll
-    for (int u = 0; u < RT; ++u) {
-      // element v of this lane: key jj = w*32 + 8*(v/4) + 4*hl + v%4 of the step
-      float x[16];
-      if constexpr (RT > 1) {
-        // Raw dot products; the scale is applied after the max-pool (rounding
-        // of scale*x is monotone in x, so max then scale gives the same bits).
-        // Only steps that reach the first row's causal edge or the key range
-        // end need the mask.
-        if (edge) {
+      for (int u = 0; u < RT; ++u)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int j = j0 + w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3);
-            x[v] = (j <= my_jmax[u] && j < Rk) ? sc[u][v] : kNegInf;
+        for (int v = 0; v < 16; ++v) sc[u][v] = 0.f;
+      if constexpr (BF16) {
+#pragma unroll
+        for (int ks = 0; ks < QREGS; ++ks)
+#pragma unroll
+          for (int u = 0; u < RT; ++u)
+            sc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cur[ks]), qf16[u][ks], sc[u], 0, 0, 0);
+      } else {
+        const bool k_ok = koff_c >= 0;
+        const float* kp = (const float*)a.k_pool + (k_ok ? koff_c : 0) + hl;
+#pragma unroll
+        for (int ks = 0; ks < QREGS; ++ks) {
+          const float kv = k_ok ? kp[2 * ks] : 0.f;
+#pragma unroll
+          for (int u = 0; u < RT; ++u) sc[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv, qf32[u][ks], sc[u], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < RT; ++u) {
+        // element v of this lane: key jj = w*32 + 8*(v/4) + 4*hl + v%4 of the step
+        float x[16];
+        if constexpr (RT > 1) {
+          // Raw dot products; the scale is applied after the max-pool (rounding
+          // of scale*x is monotone in x, so max then scale gives the same bits).
+          // Only steps that reach the first row's causal edge or the key range
+          // end need the mask.
+          if (edge) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int j = j0 + w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3);
+              x[v] = (j <= my_jmax[u] && j < Rk) ? sc[u][v] : kNegInf;
+            }
+          } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) x[v] = sc[u][v];
           }
         } else {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) x[v] = sc[u][v];
+          for (int v = 0; v < 16; ++v) {
+            const int j = j0 + w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3);
+            x[v] = (j <= my_jmax[u] && j < Rk) ? sc[u][v] * a.scale : kNegInf;
+          }
         }
-      } else {
+        if constexpr (RT > 1) {
+          // blocks of 4..32 keys lie inside one wave's 32 keys: maxima in
+          // registers, the two lane halves exchanged with v_permlane32_swap
+          float g4[4], o4[4];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int j = j0 + w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3);
-          x[v] = (j <= my_jmax[u] && j < Rk) ? sc[u][v] * a.scale : kNegInf;
+          for (int q = 0; q < 4; ++q) g4[q] = fmaxf(fmaxf(x[4 * q], x[4 * q + 1]), fmaxf(x[4 * q + 2], x[4 * q + 3]));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(g4[q]), __float_as_uint(g4[q]), false, false);
+            o4[q] = __uint_as_float(hl ? sw[0] : sw[1]);  // the other half's value
+          }
+          const int r = r0 + u * kScoreRows + l32;
+          rmx[u] = fmaxf(rmx[u], fmaxf(fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1])),
+                                       fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3]))));
+          if (hl == 0 && r < R) {
+            const int kbase = (j0 + w * 32) / per;
+            float* srow = pst[(kbase / CB) & 1][u * kScoreRows + l32] + kbase % CB;
+            float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            int nb;
+            if (per == 4) {  // block 2q + half
+              nb = 8;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                m[2 * q] = g4[q];
+                m[2 * q + 1] = o4[q];
+              }
+            } else if (per == 8) {  // block q
+              nb = 4;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) m[q] = fmaxf(g4[q], o4[q]);
+            } else if (per == 16) {  // block q/2
+              nb = 2;
+              m[0] = fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1]));
+              m[1] = fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3]));
+            } else {  // per == 32
+              nb = 1;
+              m[0] = fmaxf(fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1])),
+                           fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3])));
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              if (i < nb) srow[i] = m[i];
+          }
+        } else {
+          float (*tl)[kScoreKeys + 1] = tile[it & 1];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) tl[l32][w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3)] = x[v];
+          __syncthreads();
+          // ---- per-block maxima of the 128-key step --------------------------
+          const int nblk = kScoreKeys / per < 1 ? 1 : kScoreKeys / per;
+          for (int i = tid; i < kScoreRows * nblk; i += kThreads) {
+            const int rr = i / nblk, bi = i % nblk;
+            const int kb = (j0 + bi * per) / per;
+            const int r = r0 + rr;
+            if (r >= R || kb >= kb_end) continue;
+            float m = kNegInf;
+            for (int e = 0; e < per; ++e) m = fmaxf(m, tl[rr][bi * per + e]);
+            P[(int64_t)r * sq.max_nk + kb] = m;
+          }
         }
       }
       if constexpr (RT > 1) {
-        // blocks of 4..32 keys lie inside one wave's 32 keys: maxima in
-        // registers, the two lane halves exchanged with v_permlane32_swap
-        float g4[4], o4[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) g4[q] = fmaxf(fmaxf(x[4 * q], x[4 * q + 1]), fmaxf(x[4 * q + 2], x[4 * q + 3]));
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(g4[q]), __float_as_uint(g4[q]), false, false);
-          o4[q] = __uint_as_float(hl ? sw[0] : sw[1]);  // the other half's value
-        }
-        const int r = r0 + u * kScoreRows + l32;
-        rmx[u] = fmaxf(rmx[u], fmaxf(fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1])),
-                                     fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3]))));
-        if (hl == 0 && r < R) {
-          const int kbase = (j0 + w * 32) / per;
-          float* srow = pst[(kbase / CB) & 1][u * kScoreRows + l32] + kbase % CB;
-          float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-          int nb;
-          if (per == 4) {  // block 2q + half
-            nb = 8;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              m[2 * q] = g4[q];
-              m[2 * q + 1] = o4[q];
-            }
-          } else if (per == 8) {  // block q
-            nb = 4;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) m[q] = fmaxf(g4[q], o4[q]);
-          } else if (per == 16) {  // block q/2
-            nb = 2;
-            m[0] = fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1]));
-            m[1] = fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3]));
-          } else {  // per == 32
-            nb = 1;
-            m[0] = fmaxf(fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1])),
-                         fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3])));
+        // last step of a chunk of CB blocks: write the chunk's rows, scaled
+        const int cks = CB * per;  // keys per chunk
+        if ((j0 + kScoreKeys) % cks == 0 || j0 + kScoreKeys >= jend) {
+          const int ch = j0 / cks;
+          __syncthreads();
+          for (int i = tid; i < ROWS * CB; i += kThreads) {
+            const int rr = i / CB, c = i % CB;
+            const int r = r0 + rr, kb = ch * CB + c;
+            if (r < R && kb < kb_end) P[(int64_t)r * sq.max_nk + kb] = pst[ch & 1][rr][c] * a.scale;
           }
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            if (i < nb) srow[i] = m[i];
-        }
-      } else {
-        float (*tl)[kScoreKeys + 1] = tile[it & 1];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) tl[l32][w * 32 + 8 * (v >> 2) + 4 * hl + (v & 3)] = x[v];
-        __syncthreads();
-        // ---- per-block maxima of the 128-key step --------------------------
-        const int nblk = kScoreKeys / per < 1 ? 1 : kScoreKeys / per;
-        for (int i = tid; i < kScoreRows * nblk; i += kThreads) {
-          const int rr = i / nblk, bi = i % nblk;
-          const int kb = (j0 + bi * per) / per;
-          const int r = r0 + rr;
-          if (r >= R || kb >= kb_end) continue;
-          float m = kNegInf;
-          for (int e = 0; e < per; ++e) m = fmaxf(m, tl[rr][bi * per + e]);
-          P[(int64_t)r * sq.max_nk + kb] = m;
         }
       }
-    }
-    if constexpr (RT > 1) {
-      // last step of a chunk of CB blocks: write the chunk's rows, scaled
-      const int cks = CB * per;  // keys per chunk
-      if ((j0 + kScoreKeys) % cks == 0 || j0 + kScoreKeys >= jend) {
-        const int ch = j0 / cks;
-        __syncthreads();
-        for (int i = tid; i < ROWS * CB; i += kThreads) {
-          const int rr = i / CB, c = i % CB;
-          const int r = r0 + rr, kb = ch * CB + c;
-          if (r < R && kb < kb_end) P[(int64_t)r * sq.max_nk + kb] = pst[ch & 1][rr][c] * a.scale;
-        }
-      }
-    }
-    if constexpr (BF16) {
-#pragma unroll
-      for (int ks = 0; ks < QREGS; ++ks) kc[ks] = kn[ks];
-    }
     koff_c = koff_n;
+  };
+  for (int j0 = 0; j0 < jend; j0 += 2 * kScoreKeys, it += 2) {
+    step(j0, it, kc, kn);
+    if (j0 + kScoreKeys < jend) step(j0 + kScoreKeys, it + 1, kn, kc);
   }
   if constexpr (RT > 1) {
     // Row maxima of P: each wave saw a quarter of every step's keys, so the
