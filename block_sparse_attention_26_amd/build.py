@@ -66,8 +66,13 @@ def build(jobs: int = 3, verbose: bool = False) -> str:
     os.makedirs(OUT, exist_ok=True)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(_compile, SOURCES))
+    # export only the C ABI (cosa_*): internal launchers stay local
+    exports = os.path.join(OUT, "exports.map")
+    with open(exports, "w") as f:
+        f.write("{ global: cosa_*; local: *; };\n")
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", f"-Wl,--version-script={exports}", "-o", tmp,
+           *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

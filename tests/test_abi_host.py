@@ -5,6 +5,8 @@ import ctypes
 import math
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -28,6 +30,11 @@ def test_header_symbols_are_exported():
     assert declared == set(cosa.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), name
+    nm = shutil.which("nm")
+    if nm:  # nothing else is exported: internal launchers stay local
+        out = subprocess.run([nm, "-D", "--defined-only", cosa.library_path()], capture_output=True, text=True).stdout
+        exported = {l.split()[-1] for l in out.splitlines() if l.strip() and l.split()[-2] in ("T", "t")}
+        assert exported == declared, sorted(exported ^ declared)
     assert cosa.cosa_version() >= 100
     assert cosa.cosa_status_string(0) == "success"
 
