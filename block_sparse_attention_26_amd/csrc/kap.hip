@@ -215,12 +215,16 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
   }
 
   const int jend = kb_end * per;  // pooled keys covered
+  // the sequence's block table row, staged once (the fragment addresses of a
+  // step then need no dependent global load)
+  __shared__ int32_t ptab[kMaxSortBlocks];
+  for (int i = tid; i < kb_end; i += kThreads) ptab[i] = sq.block_table[(int64_t)b * sq.max_blocks_k + i];
+  __syncthreads();
   // this lane's key row (A operand) of the step at j0: element offset, or -1
   auto key_off = [&](int j0) -> int64_t {
     const int jk = j0 + w * 32 + l32;
     if (!(jk < Rk && jk < jend)) return -1;
-    const int kbk = jk / per;
-    const int page = sq.block_table[(int64_t)b * sq.max_blocks_k + kbk];
+    const int page = ptab[jk / per];
     return (int64_t)((((size_t)page * sq.h_kv + g) * per) + jk % per) * D;
   };
   // the next step's K fragments are loaded while the current step computes
