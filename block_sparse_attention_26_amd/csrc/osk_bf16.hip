@@ -46,40 +46,44 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// Maxima as llvm.maximum (v_maximum3_f32 on gfx950). Through fmaxf the
+// compiler first quiets every operand it cannot prove free of signaling NaNs
+// (an extra v_max_f32 x, x, x each); maximum needs no quieting because it
+// propagates NaN, which the score maxima may do: a NaN score only comes from a
+// NaN input, and then the row's result is NaN either way.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
+
 // x combined with lane l ^ 32's x (v_permlane32_swap exchanges the halves)
 __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// max with a DPP-permuted copy of x (within rows of 16 lanes)
+// max of x over lanes 0..31, valid in lane 0: within each row of 16 lanes a
+// max with a DPP-permuted copy (pair swap, quad swap, half-row mirror, row
+// mirror) leaves the row's maximum in every lane; then rows 0 and 1 combine.
 template <int CTRL>
 __device__ __forceinline__ float dpp_max(float x) {
-  return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false)));
+  return vmax(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false)));
 }
-
-// max of x over lanes 0..31, uniform: quad butterflies, half-row and row
-// mirrors, then the two 16-lane rows
-__device__ __forceinline__ float wave_max32(float x) {
+__device__ __forceinline__ float wave_max32_lane0(float x) {
   x = dpp_max<0xB1>(x);   // quad_perm [1,0,3,2]
   x = dpp_max<0x4E>(x);   // quad_perm [2,3,0,1]
   x = dpp_max<0x141>(x);  // row_half_mirror
   x = dpp_max<0x140>(x);  // row_mirror
-  return fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)),
-               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16)));
+  return vmax(x, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16)));
 }
-
-__device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // max of the 16 values of an accumulator, as a shallow tree
 __device__ __forceinline__ float max16(const f32x16& v) {
-  const float t0 = fmax3(v[0], v[1], v[2]), t1 = fmax3(v[3], v[4], v[5]), t2 = fmax3(v[6], v[7], v[8]);
-  const float t3 = fmax3(v[9], v[10], v[11]), t4 = fmax3(v[12], v[13], v[14]);
-  return fmaxf(fmax3(t0, t1, t2), fmax3(t3, t4, v[15]));
+  const float t0 = vmax3(v[0], v[1], v[2]), t1 = vmax3(v[3], v[4], v[5]), t2 = vmax3(v[6], v[7], v[8]);
+  const float t3 = vmax3(v[9], v[10], v[11]), t4 = vmax3(v[12], v[13], v[14]);
+  return vmax(vmax3(t0, t1, t2), vmax3(t3, t4, v[15]));
 }
 
 template <int D, int BLK>
@@ -384,12 +388,12 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
     }
     float m_loc = max16(s[0]);
 #pragma unroll
-    for (int kt = 1; kt < KT; ++kt) m_loc = fmaxf(m_loc, max16(s[kt]));
+    for (int kt = 1; kt < KT; ++kt) m_loc = vmax(m_loc, max16(s[kt]));
     m_loc = max_xor32(m_loc);
     if constexpr (!DENSE) {
       if (a.skip_on) {
         float diff = (row_valid && m_loc != kNegInf) ? m_loc - m_run : kNegInf;
-        diff = wave_max32(diff);
+        diff = wave_max32_lane0(diff);
         if (lane == 0) red[w] = diff;
       }
     }
@@ -400,7 +404,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
       if (a.skip_on) {
         float worst = red[0];
 #pragma unroll
-        for (int i = 1; i < NW; ++i) worst = fmaxf(worst, red[i]);
+        for (int i = 1; i < NW; ++i) worst = vmax(worst, red[i]);
         skip = __builtin_amdgcn_readfirstlane(worst < a.skip_thr_raw ? 1 : 0) != 0;
       }
     }
@@ -420,7 +424,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
         for (int i = tid; i < (BLK - nvalid) * ROWB / 16; i += Gm::THREADS) z[i] = make_uint4(0, 0, 0, 0);
         __syncthreads();
       }
-      const float m_new = fmaxf(m_run, m_loc);
+      const float m_new = vmax(m_run, m_loc);
       const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
       const float mc = (m_new == kNegInf) ? 0.f : m_new * c2;
       if (__any(alpha != 1.f)) {  // rescale only when some row's max moved
