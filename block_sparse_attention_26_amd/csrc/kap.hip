@@ -5,7 +5,8 @@
 // §2.2 Stage 1, in the page's order:
 //   block ranking - downsample Q and K (kap_pool_q / kap_pool_k: mean over p
 //       tokens), approximate scores and MaxPool over the keys of each KV block
-//       (kap_score: MFMA GEMM with the per-block max fused into its epilogue),
+//       (kap_score_grp / kap_score: MFMA GEMM with the per-block max fused
+//       into its epilogue),
 //       MaxNorm (kap_rank_sort: exp(P - row max));
 //   HRM flag generation - blocks that attain some pooled row's max, united
 //       over the query heads of a KV group (the GQA union follows the
@@ -21,6 +22,8 @@
 // the same P. Floating-point contraction is disabled for that code.
 #include <math.h>
 
+#include <type_traits>
+
 #include "cosa_internal.h"
 
 namespace cosa {
@@ -28,6 +31,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kThreads = 256;
@@ -132,13 +136,17 @@ __global__ __launch_bounds__(kThreads) void kap_pool_k(KapArgs a) {
   }
 }
 
+// llvm.maximum (v_maximum3_f32 on gfx950): unlike fmaxf it needs no quieting
+// copy of operands the compiler cannot prove free of signaling NaNs
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // ---- proxy scores with fused MaxPool (readings R2-R4) ----------------------
 // One workgroup per (sequence, query head, tile of 32*RT pooled rows), longest
 // tiles first. Each of the 4 waves computes 32-key x 32-row tiles of
 // S^T = Kpool . Qpool^T per step (128 pooled keys per step), one per row tile
 // against the same K fragments (loaded one step ahead). Blocks of 4..32 pooled
-// keys are reduced to their maxima in registers (RT = 2); other block sizes go
-// through LDS (RT = 1).
+// keys are reduced to their maxima in registers (RT = 2; the fp32 path, bf16
+// takes the group form below); other block sizes go through LDS (RT = 1).
 constexpr int kScoreRows = 32;
 constexpr int kScoreKeys = 128;
 
@@ -306,15 +314,15 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
           // registers, the two lane halves exchanged with v_permlane32_swap
           float g4[4], o4[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) g4[q] = fmaxf(fmaxf(x[4 * q], x[4 * q + 1]), fmaxf(x[4 * q + 2], x[4 * q + 3]));
+          for (int q = 0; q < 4; ++q) g4[q] = vmax(vmax(x[4 * q], x[4 * q + 1]), vmax(x[4 * q + 2], x[4 * q + 3]));
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(g4[q]), __float_as_uint(g4[q]), false, false);
             o4[q] = __uint_as_float(hl ? sw[0] : sw[1]);  // the other half's value
           }
           const int r = r0 + u * kScoreRows + l32;
-          rmx[u] = fmaxf(rmx[u], fmaxf(fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1])),
-                                       fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3]))));
+          rmx[u] = vmax(rmx[u], vmax(vmax(vmax(g4[0], o4[0]), vmax(g4[1], o4[1])),
+                                       vmax(vmax(g4[2], o4[2]), vmax(g4[3], o4[3]))));
           if (hl == 0 && r < R) {
             const int kbase = (j0 + w * 32) / per;
             float* srow = pst[(kbase / CB) & 1][u * kScoreRows + l32] + kbase % CB;
@@ -330,15 +338,15 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
             } else if (per == 8) {  // block q
               nb = 4;
 #pragma unroll
-              for (int q = 0; q < 4; ++q) m[q] = fmaxf(g4[q], o4[q]);
+              for (int q = 0; q < 4; ++q) m[q] = vmax(g4[q], o4[q]);
             } else if (per == 16) {  // block q/2
               nb = 2;
-              m[0] = fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1]));
-              m[1] = fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3]));
+              m[0] = vmax(vmax(g4[0], o4[0]), vmax(g4[1], o4[1]));
+              m[1] = vmax(vmax(g4[2], o4[2]), vmax(g4[3], o4[3]));
             } else {  // per == 32
               nb = 1;
-              m[0] = fmaxf(fmaxf(fmaxf(g4[0], o4[0]), fmaxf(g4[1], o4[1])),
-                           fmaxf(fmaxf(g4[2], o4[2]), fmaxf(g4[3], o4[3])));
+              m[0] = vmax(vmax(vmax(g4[0], o4[0]), vmax(g4[1], o4[1])),
+                           vmax(vmax(g4[2], o4[2]), vmax(g4[3], o4[3])));
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -409,6 +417,230 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
       if (r >= R || kb >= kb_end) P[(int64_t)r * sq.max_nk + kb] = kNegInf;
     }
   }
+}
+
+// ---- proxy scores, group form (bf16, blocks of 4..32 pooled keys) ----------
+// One workgroup per (sequence, KV group, four (query head, 32-row tile)
+// pairs), pairs numbered tile-major so a workgroup's waves share a row tile
+// when G >= 4 and hold adjacent tiles otherwise; longest tiles first. Each
+// step's 128 pooled keys are copied once into LDS (global_load_lds, rows
+// XOR-swizzled by (row mod 16) through the choice of each lane's source
+// chunk) and shared by the four waves. Each wave forms S^T = Kpool . Qpool^T for its 32 rows
+// against all keys of a step (two 32-key tiles), so its row maxima need no
+// combining across waves, and writes the step's block maxima (times the
+// scale: rounding of scale * x is monotone in x) straight from registers.
+// Steps are 64 keys in a ring of NSTAGE LDS stages: the copy of step
+// t + NSTAGE - 1 is issued when step t starts.
+template <int D, int BLK>
+__global__ __launch_bounds__(kThreads, 2) void kap_score_grp(KapArgs a) {
+  constexpr int STEP = 64;               // pooled keys per step
+  constexpr int NSTAGE = 3;              // LDS ring (three workgroups per CU at d = 128)
+  constexpr int ROWB = D * 2;            // bytes per pooled key row
+  constexpr int STAGE = STEP * ROWB;     // bytes per step tile
+  constexpr int CH = D / 8;              // 16-byte chunks per row
+  constexpr int RPC = 1024 / ROWB;       // rows per 1 KB copy
+  constexpr int CPW = STAGE / 1024 / 4;  // copies per wave per step
+  constexpr int QREGS = D / 16;
+  constexpr int KT = STEP / 32;
+  __shared__ __attribute__((aligned(1024))) unsigned char kst[NSTAGE][STAGE];
+  extern __shared__ int32_t ptab[];      // the sequence's block-table row (dynamic)
+  const SeqArgs& sq = a.seq;
+  const int G = sq.group;
+  const int ntile = (a.max_nr + 31) / 32;
+  const int npb = (G * ntile + 3) / 4;   // pair blocks per (sequence, group)
+  const int64_t bid = blockIdx.x;
+  const int g = (int)(bid % sq.h_kv);
+  int64_t rest = bid / sq.h_kv;
+  const int b = (int)(rest % sq.batch);
+  const int pb = npb - 1 - (int)(rest / sq.batch);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int q0 = __builtin_amdgcn_readfirstlane(sq.cu_seqlens_q[b]);
+  const int Lq = __builtin_amdgcn_readfirstlane(sq.cu_seqlens_q[b + 1]) - q0;
+  const int Lk = __builtin_amdgcn_readfirstlane(sq.seqlens_k[b]);
+  const int off = Lk - Lq;
+  const int p = a.pool;
+  const int per = BLK / p;               // pooled keys per KV block: 4, 8, 16 or 32
+  const int lper = __builtin_ctz(per);
+  const int R = (Lq + p - 1) / p;
+  const int Rk = (Lk + p - 1) / p;
+  const int nk = (Lk + BLK - 1) / BLK;
+  // this wave's pair
+  const int pair = pb * 4 + w;
+  const int rt = pair / G;
+  const int h = g * G + pair % G;
+  const bool wave_on = pair < G * ntile;
+  const int r0 = rt * 32;
+  float* P = a.scores + (((int64_t)b * sq.h_q + h) * a.max_nr) * sq.max_nk;
+  // -inf for a wave's rows and blocks it does not compute (export mode)
+  auto fill_rest = [&](int kb_from) {
+    if (!a.fill_scores || !wave_on) return;
+    for (int i = lane; i < 32 * sq.max_nk; i += 64) {
+      const int r = r0 + i / sq.max_nk, kb = i % sq.max_nk;
+      if (r < a.max_nr && (r >= R || kb >= kb_from)) P[(int64_t)r * sq.max_nk + kb] = kNegInf;
+    }
+  };
+  // the workgroup's last pair holds its furthest rows
+  const int rt_last = min(pb * 4 + 3, G * ntile - 1) / G;
+  const int r_last = min(rt_last * 32 + 32, R) - 1;
+  if (pb * 4 / G * 32 >= R) {  // no row of this sequence here
+    fill_rest(0);
+    return;
+  }
+  const int qb_last = r_last >> lper;
+  const int kb_end = min((off + min(qb_last * BLK + BLK - 1, Lq - 1)) / BLK + 1, nk);
+  const int jend = kb_end * per;  // pooled keys covered
+
+  for (int i = tid; i < kb_end; i += kThreads) ptab[i] = sq.block_table[(int64_t)b * sq.max_blocks_k + i];
+
+  // query fragments (B operand) of this wave's 32 rows
+  const int my_r = r0 + l32;
+  const bool r_ok = wave_on && my_r < R;
+  const int my_jmax = r_ok ? (off + min(my_r * p + p - 1, Lq - 1)) / p : -1;
+  const int jmax_first = wave_on && r0 < R ? (off + min(r0 * p + p - 1, Lq - 1)) / p : -1;
+  bf16x8 qf[QREGS];
+  {
+    const size_t qoff = (((size_t)b * a.max_nr + (r_ok ? my_r : 0)) * sq.h_q + (wave_on ? h : 0)) * D;
+    const uint16_t* qp = (const uint16_t*)a.q_pool + qoff + hl * 8;
+#pragma unroll
+    for (int ks = 0; ks < QREGS; ++ks) {
+      const uint4 x = r_ok ? *(const uint4*)(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+      qf[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  __syncthreads();  // ptab staged
+
+  // copy n of this wave fills stage bytes [(w*CPW + n) * 1024, +1024): row
+  // cr = (w*CPW + n)*RPC + lane/CH of the step, physical chunk lane%CH holding
+  // logical chunk (lane%CH) ^ (cr % CH). A row past the covered blocks reads
+  // the last covered block (its scores are masked).
+  const unsigned char* kpool = (const unsigned char*)a.k_pool + (size_t)g * per * ROWB;
+  const size_t page_bytes = (size_t)sq.h_kv * per * ROWB;
+  uint32_t c_off[CPW];
+  int c_blk[CPW];
+#pragma unroll
+  for (int n = 0; n < CPW; ++n) {
+    const int cr = (w * CPW + n) * RPC + lane / CH;
+    c_off[n] = (uint32_t)((cr & (per - 1)) * ROWB + (((lane % CH) ^ (cr % CH)) << 4));
+    c_blk[n] = cr >> lper;
+  }
+  auto issue = [&](int j0, int stage) {
+#pragma unroll
+    for (int n = 0; n < CPW; ++n) {
+      const int kbq = min((j0 >> lper) + c_blk[n], kb_end - 1);
+      const unsigned page = min((unsigned)ptab[kbq], (unsigned)sq.num_pages - 1u);  // a corrupt entry stays in the pool
+      const unsigned char* src = kpool + (size_t)page * page_bytes + c_off[n];
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(kst[stage] + (w * CPW + n) * 1024), 16, 0, 0);
+    }
+  };
+
+  // A operand: key row kt*32 + l32, logical chunk 2*ks + hl
+  const int k_swz = l32 % CH;
+  float rmx = kNegInf;       // raw row maximum over the computed keys
+  // s_waitcnt with vmcnt <= (NSTAGE-2)*CPW (expcnt and lgkmcnt at their
+  // maxima): vector memory operations complete in issue order, and when the
+  // copies of the NSTAGE-2 following steps were issued after this step's, at
+  // least that many operations are newer than it
+  constexpr int AHEAD = NSTAGE - 2;
+  constexpr int kWaitAhead = (AHEAD * CPW) | (7 << 4) | (0xF << 8);
+  static_assert(AHEAD * CPW < 16, "vmcnt field");
+#pragma unroll
+  for (int t = 0; t < NSTAGE - 1; ++t)
+    if (t * STEP < jend) issue(t * STEP, t);
+  int stage = 0;
+  for (int j0 = 0; j0 < jend; j0 += STEP, stage = stage + 1 == NSTAGE ? 0 : stage + 1) {
+    if (j0 + AHEAD * STEP < jend)
+      __builtin_amdgcn_s_waitcnt(kWaitAhead);
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // this step's tile landed; every wave is done with the previous step's stage
+    if (j0 + (NSTAGE - 1) * STEP < jend) issue(j0 + (NSTAGE - 1) * STEP, stage == 0 ? NSTAGE - 1 : stage - 1);
+    if (!wave_on) continue;
+    const unsigned char* kl = kst[stage] + l32 * ROWB;
+    f32x16 sc[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sc[kt][v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < QREGS; ++ks) {
+      bf16x8 kf[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) kf[kt] = *(const bf16x8*)(kl + kt * 32 * ROWB + (((2 * ks + hl) ^ k_swz) << 4));
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt], qf[ks], sc[kt], 0, 0, 0);
+    }
+    // element v of tile kt: key j0 + kt*32 + 8*(v/4) + 4*hl + v%4; only steps
+    // that reach the first row's causal edge or the key range end need the mask
+    const bool edge = j0 + STEP - 1 > jmax_first || j0 + STEP > Rk;
+    float bm[STEP / 4];  // block maxima of the step (NB used)
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      if (edge) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int j = j0 + kt * 32 + 8 * (v >> 2) + 4 * hl + (v & 3);
+          if (!(j <= my_jmax && j < Rk)) sc[kt][v] = kNegInf;
+        }
+      }
+      // maxima of the lane's four groups of 4 keys, and of the other half's
+      float g4[4], o4[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) g4[q] = vmax(vmax(sc[kt][4 * q], sc[kt][4 * q + 1]), vmax(sc[kt][4 * q + 2], sc[kt][4 * q + 3]));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(g4[q]), __float_as_uint(g4[q]), false, false);
+        o4[q] = __uint_as_float(hl ? sw[0] : sw[1]);
+      }
+      // keys 8q..8q+3 and 8q+4..8q+7 of the tile
+      float lo[4], hi[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        lo[q] = hl ? o4[q] : g4[q];
+        hi[q] = hl ? g4[q] : o4[q];
+      }
+      const float t01 = vmax(vmax(lo[0], hi[0]), vmax(lo[1], hi[1]));
+      const float t23 = vmax(vmax(lo[2], hi[2]), vmax(lo[3], hi[3]));
+      rmx = vmax(rmx, vmax(t01, t23));
+      if (per == 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bm[kt * 8 + 2 * q] = lo[q];
+          bm[kt * 8 + 2 * q + 1] = hi[q];
+        }
+      } else if (per == 8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bm[kt * 4 + q] = vmax(lo[q], hi[q]);
+      } else if (per == 16) {
+        bm[kt * 2] = t01;
+        bm[kt * 2 + 1] = t23;
+      } else {
+        bm[kt] = vmax(t01, t23);
+      }
+    }
+    // the step's NB block maxima of this lane's row: the two lane halves
+    // write one half each
+    auto store = [&](auto nb_c) {
+      constexpr int HALF = decltype(nb_c)::value / 2;
+      float* prow = P + (int64_t)my_r * sq.max_nk + (j0 >> lper) + hl * HALF;
+      const int room = kb_end - (j0 >> lper) - hl * HALF;  // blocks of this half still covered
+#pragma unroll
+      for (int i = 0; i < HALF; ++i)
+        if (i < room) prow[i] = (hl ? bm[HALF + i] : bm[i]) * a.scale;
+    };
+    if (r_ok) {
+      if (per == 4) store(std::integral_constant<int, STEP / 4>{});
+      else if (per == 8) store(std::integral_constant<int, STEP / 8>{});
+      else if (per == 16) store(std::integral_constant<int, STEP / 16>{});
+      else store(std::integral_constant<int, STEP / 32>{});
+    }
+  }
+  if (wave_on) {
+    if (a.row_max && hl == 0 && r_ok) a.row_max[((int64_t)b * sq.h_q + h) * a.max_nr + my_r] = rmx * a.scale;
+    fill_rest(kb_end);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no copy is in flight when the workgroup's LDS is released
 }
 
 // ---- exp32: the proxy's exponential, as specified ---------------------------
@@ -780,10 +1012,18 @@ hipError_t launch_all(const KapArgs& a, hipStream_t stream) {
     const int64_t g3 = nchunk * sq.h_kv * sq.batch;
     if constexpr (BF16)
       hipLaunchKernelGGL((kap_score_decode<D, BLK>), dim3((unsigned)g3), dim3(kThreads), 0, stream, a);
-  } else if (per >= 4 && per <= 32) {  // block maxima in registers: two row tiles share each K load
+  } else if (BF16 && per >= 4 && per <= 32) {  // group form: pooled K staged once per KV group
+    const int64_t ntile = (a.max_nr + 31) / 32;
+    const int64_t npb = (sq.group * ntile + 3) / 4;
+    const int64_t g3 = npb * sq.batch * sq.h_kv;
+    if constexpr (BF16)
+      hipLaunchKernelGGL((kap_score_grp<D, BLK>), dim3((unsigned)g3), dim3(kThreads),
+                         (size_t)sq.max_nk * sizeof(int32_t), stream, a);
+  } else if (per >= 4 && per <= 32) {  // fp32: block maxima in registers, two row tiles share each K load
     const int64_t ntile = (a.max_nr + 2 * kScoreRows - 1) / (2 * kScoreRows);
     const int64_t g3 = ntile * sq.batch * sq.h_q;
-    hipLaunchKernelGGL((kap_score<BF16, D, BLK, 2>), dim3((unsigned)g3), dim3(kThreads), 0, stream, a);
+    if constexpr (!BF16)
+      hipLaunchKernelGGL((kap_score<BF16, D, BLK, 2>), dim3((unsigned)g3), dim3(kThreads), 0, stream, a);
   } else {
     const int64_t ntile = (a.max_nr + kScoreRows - 1) / kScoreRows;
     const int64_t g3 = ntile * sq.batch * sq.h_q;
