@@ -107,7 +107,7 @@ def cpu_baseline(case, kap_count, seconds_target=20.0):
     t_kap = time.perf_counter() - t0
     nq = layout.cdiv(T, B)
     t_osk, done_blocks, done_q = 0.0, 0, []
-    stride = max(1, nq // 64)
+    stride = max(1, nq // 128)  # up to 128 evenly spaced query blocks
     for qb in list(range(nq - 1, -1, -stride)):
         if t_osk > seconds_target / 2:
             break

@@ -7,8 +7,9 @@
   sets identical outside a 1e-3-nat band around the threshold, O within
   2e-2 max / 2e-3 mean (bf16) or 1e-4 (fp32) of the fp64 oracle.
 * Dense: O and lse against the fp64 dense oracle.
-Cases span several tiles, ragged tails, GQA 1/4/8, chunked offsets, shuffled
-NaN-poisoned page pools and packed ragged batches.
+Cases span several tiles, ragged tails, chunked offsets, shuffled
+NaN-poisoned page pools and packed ragged batches; GQA groups of 1, 2, 3, 4,
+8 and 16.
 """
 import math
 
@@ -48,6 +49,11 @@ CASES = {
     "bf16-b128-p4": _lr("bf16-b128-p4", 21, [800], [1000], hq=4, hkv=2, d=128, B=128, p=4),
     "bf16-b64-p32": _lr("bf16-b64-p32", 22, [700], hq=2, hkv=1, d=64, B=64, p=32),
     "bf16-b128-p1": _lr("bf16-b128-p1", 23, [600], hq=2, hkv=2, d=64, B=128, p=1),
+    # odd and wide query groups: the proxy's score pass groups four (head,
+    # row tile) pairs per workgroup, which straddle row tiles when G = 3
+    "bf16-gqa3-b64-p16": _lr("bf16-gqa3-b64-p16", 24, [1500, 400], [1500, 900], hq=6, hkv=2, d=128, B=64, p=16,
+                             per_sequence_seeds=True),
+    "bf16-gqa16": _lr("bf16-gqa16", 25, [900], hq=16, hkv=1, d=128, B=128, p=16),
 }
 
 
