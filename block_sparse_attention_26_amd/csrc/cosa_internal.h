@@ -10,6 +10,7 @@ namespace cosa {
 // Workgroups are dispatched round-robin over the MI355X's 8 XCDs (each with
 // its own L2); launch mappings group units that share K/V pages per XCD.
 constexpr int kNumXcd = 8;
+constexpr int kNumCu = 256;  // compute units of one MI355X
 
 // Largest KV-block count per sequence the proxy's in-LDS sort handles.
 constexpr int kMaxSortBlocks = 4096;
@@ -67,6 +68,7 @@ struct KapArgs {
   float scale;
   int32_t keys_pooled;     // k_pool already holds the pooled keys: skip key pooling
   int32_t pool_last_only;  // key pooling: only the last KV block of each sequence
+  int32_t score_splits;    // score pass: workgroups sharing one key range (set by the launcher)
 };
 
 // The proxy scores a problem with one pooled query row per sequence (a decode

@@ -22,6 +22,8 @@
 // the same P. Floating-point contraction is disabled for that code.
 #include <math.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 #include "cosa_internal.h"
@@ -429,6 +431,10 @@ __global__ __launch_bounds__(kThreads) void kap_score(KapArgs a) {
 // against all keys of a step (two 32-key tiles), so its row maxima need no
 // combining across waves, and writes the step's block maxima (times the
 // scale: rounding of scale * x is monotone in x) straight from registers.
+// When the pairs alone give too few workgroups for the chip (a short query
+// chunk over a long cache), score_splits workgroups share a pair set, each
+// taking a contiguous share of its steps, and the row maxima are left to the
+// rank pass.
 // Steps are 64 keys in a ring of NSTAGE LDS stages: the copy of step
 // t + NSTAGE - 1 is issued when step t starts.
 template <int D, int BLK>
@@ -448,7 +454,9 @@ __global__ __launch_bounds__(kThreads, 2) void kap_score_grp(KapArgs a) {
   const int G = sq.group;
   const int ntile = (a.max_nr + 31) / 32;
   const int npb = (G * ntile + 3) / 4;   // pair blocks per (sequence, group)
-  const int64_t bid = blockIdx.x;
+  const int nsplit = a.score_splits;
+  const int split = (int)(blockIdx.x % nsplit);
+  const int64_t bid = blockIdx.x / nsplit;
   const int g = (int)(bid % sq.h_kv);
   int64_t rest = bid / sq.h_kv;
   const int b = (int)(rest % sq.batch);
@@ -475,7 +483,7 @@ __global__ __launch_bounds__(kThreads, 2) void kap_score_grp(KapArgs a) {
   float* P = a.scores + (((int64_t)b * sq.h_q + h) * a.max_nr) * sq.max_nk;
   // -inf for a wave's rows and blocks it does not compute (export mode)
   auto fill_rest = [&](int kb_from) {
-    if (!a.fill_scores || !wave_on) return;
+    if (!a.fill_scores || !wave_on || split != 0) return;
     for (int i = lane; i < 32 * sq.max_nk; i += 64) {
       const int r = r0 + i / sq.max_nk, kb = i % sq.max_nk;
       if (r < a.max_nr && (r >= R || kb >= kb_from)) P[(int64_t)r * sq.max_nk + kb] = kNegInf;
@@ -491,6 +499,14 @@ __global__ __launch_bounds__(kThreads, 2) void kap_score_grp(KapArgs a) {
   const int qb_last = r_last >> lper;
   const int kb_end = min((off + min(qb_last * BLK + BLK - 1, Lq - 1)) / BLK + 1, nk);
   const int jend = kb_end * per;  // pooled keys covered
+  // this workgroup's share of the steps
+  const int nsteps = (jend + STEP - 1) / STEP;
+  const int j_lo = (int)((int64_t)split * nsteps / nsplit) * STEP;
+  const int j_hi = min((int)((int64_t)(split + 1) * nsteps / nsplit) * STEP, jend);
+  if (j_lo >= j_hi) {
+    fill_rest(kb_end);
+    return;
+  }
 
   for (int i = tid; i < kb_end; i += kThreads) ptab[i] = sq.block_table[(int64_t)b * sq.max_blocks_k + i];
 
@@ -547,15 +563,15 @@ __global__ __launch_bounds__(kThreads, 2) void kap_score_grp(KapArgs a) {
   static_assert(AHEAD * CPW < 16, "vmcnt field");
 #pragma unroll
   for (int t = 0; t < NSTAGE - 1; ++t)
-    if (t * STEP < jend) issue(t * STEP, t);
+    if (j_lo + t * STEP < j_hi) issue(j_lo + t * STEP, t);
   int stage = 0;
-  for (int j0 = 0; j0 < jend; j0 += STEP, stage = stage + 1 == NSTAGE ? 0 : stage + 1) {
-    if (j0 + AHEAD * STEP < jend)
+  for (int j0 = j_lo; j0 < j_hi; j0 += STEP, stage = stage + 1 == NSTAGE ? 0 : stage + 1) {
+    if (j0 + AHEAD * STEP < j_hi)
       __builtin_amdgcn_s_waitcnt(kWaitAhead);
     else
       __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // this step's tile landed; every wave is done with the previous step's stage
-    if (j0 + (NSTAGE - 1) * STEP < jend) issue(j0 + (NSTAGE - 1) * STEP, stage == 0 ? NSTAGE - 1 : stage - 1);
+    if (j0 + (NSTAGE - 1) * STEP < j_hi) issue(j0 + (NSTAGE - 1) * STEP, stage == 0 ? NSTAGE - 1 : stage - 1);
     if (!wave_on) continue;
     const unsigned char* kl = kst[stage] + l32 * ROWB;
     f32x16 sc[KT];
@@ -997,6 +1013,8 @@ __global__ __launch_bounds__(kThreads) void kap_rank_sort(KapArgs a) {
 template <bool BF16, int D, int BLK>
 hipError_t launch_all(const KapArgs& a, hipStream_t stream) {
   const SeqArgs& sq = a.seq;
+  KapArgs ra = a;  // the score and rank passes' arguments (split score pass: no row maxima)
+  ra.score_splits = 1;
   const int64_t g1 = (int64_t)sq.batch * a.max_nr;
   hipLaunchKernelGGL((kap_pool_q<BF16, D>), dim3((unsigned)g1), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
@@ -1016,9 +1034,16 @@ hipError_t launch_all(const KapArgs& a, hipStream_t stream) {
     const int64_t ntile = (a.max_nr + 31) / 32;
     const int64_t npb = (sq.group * ntile + 3) / 4;
     const int64_t g3 = npb * sq.batch * sq.h_kv;
+    // a grid of fewer than two workgroups per CU splits each pair set's keys
+    // (at most 8 ways); the rank pass then takes the row maxima from P
+    const int64_t nsplit = std::min<int64_t>(8, std::max<int64_t>(1, (2 * kNumCu + g3 - 1) / g3));
+    if (nsplit > 1) {
+      ra.row_max = nullptr;
+      ra.score_splits = (int32_t)nsplit;
+    }
     if constexpr (BF16)
-      hipLaunchKernelGGL((kap_score_grp<D, BLK>), dim3((unsigned)g3), dim3(kThreads),
-                         (size_t)sq.max_nk * sizeof(int32_t), stream, a);
+      hipLaunchKernelGGL((kap_score_grp<D, BLK>), dim3((unsigned)(g3 * nsplit)), dim3(kThreads),
+                         (size_t)sq.max_nk * sizeof(int32_t), stream, ra);
   } else if (per >= 4 && per <= 32) {  // fp32: block maxima in registers, two row tiles share each K load
     const int64_t ntile = (a.max_nr + 2 * kScoreRows - 1) / (2 * kScoreRows);
     const int64_t g3 = ntile * sq.batch * sq.h_q;
@@ -1031,7 +1056,7 @@ hipError_t launch_all(const KapArgs& a, hipStream_t stream) {
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t g4 = (int64_t)sq.max_nq * sq.batch * sq.h_kv;
-  hipLaunchKernelGGL((kap_rank_sort<BLK>), dim3((unsigned)g4), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((kap_rank_sort<BLK>), dim3((unsigned)g4), dim3(kThreads), 0, stream, ra);
   return hipGetLastError();
 }
 
