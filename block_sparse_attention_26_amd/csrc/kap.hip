@@ -107,27 +107,41 @@ __global__ __launch_bounds__(kThreads) void kap_pool_q(KapArgs a) {
 template <bool BF16, int D, int BLK>
 __global__ __launch_bounds__(kThreads) void kap_pool_k(KapArgs a) {
   const SeqArgs& sq = a.seq;
-  // all blocks, or (decode) only the last block of each sequence
-  const int b = a.pool_last_only ? blockIdx.x : blockIdx.x / sq.max_nk;
+  // every block (one workgroup per (sequence, block)), or, in decode, only
+  // the last block of each sequence (one workgroup per (sequence, KV head))
+  const bool last = a.pool_last_only != 0;
+  const int b = last ? blockIdx.x / sq.h_kv : blockIdx.x / sq.max_nk;
   const int Lk = sq.seqlens_k[b];
-  const int kb = a.pool_last_only ? (Lk - 1) / BLK : blockIdx.x % sq.max_nk;
+  const int kb = last ? (Lk - 1) / BLK : blockIdx.x % sq.max_nk;
   if (Lk <= 0 || kb * BLK >= Lk) return;
   const int page = sq.block_table[(int64_t)b * sq.max_blocks_k + kb];
   if ((unsigned)page >= (unsigned)sq.num_pages) return;
   const int nvalid = min(BLK, Lk - kb * BLK);
   const int per = BLK / a.pool;  // pooled slots per page
   constexpr int CH = D / 8;
-  const int chunks = sq.h_kv * per * CH;
+  const int chunks = (last ? 1 : sq.h_kv) * per * CH;
   for (int c = threadIdx.x; c < chunks; c += kThreads) {
     const int dch = c % CH;
     const int slot = (c / CH) % per;
-    const int g = c / (CH * per);
+    const int g = last ? (int)(blockIdx.x % sq.h_kv) : c / (CH * per);
     const int lo = slot * a.pool;
     const int hi = min(lo + a.pool, nvalid);
+    const size_t row0 = ((size_t)page * sq.h_kv + g) * BLK;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int tok = lo; tok < hi; ++tok) {
+    // four tokens' loads in flight at a time; the sum stays in token order
+    int tok = lo;
+    for (; tok + 4 <= hi; tok += 4) {
+      float x[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load8<BF16>(a.k, (row0 + tok + u) * D + dch * 8, x[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += x[u][i];
+    }
+    for (; tok < hi; ++tok) {
       float x[8];
-      load8<BF16>(a.k, (((size_t)page * sq.h_kv + g) * BLK + tok) * D + dch * 8, x);
+      load8<BF16>(a.k, (row0 + tok) * D + dch * 8, x);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += x[i];
     }
@@ -688,7 +702,7 @@ constexpr int kMaxRankRows = 4096;  // G * (B/p) pooled rows per list
 // G of 32 columns used), so one workgroup scores a chunk of kDecodeKeys
 // pooled keys for the whole group; blocks of 4..32 pooled keys are reduced in
 // registers as in kap_score. Row maxima are left to the rank pass.
-constexpr int kDecodeKeys = 1024;
+constexpr int kDecodeKeys = 512;
 
 template <int D, int BLK>
 __global__ __launch_bounds__(kThreads) void kap_score_decode(KapArgs a) {
@@ -1074,7 +1088,7 @@ hipError_t launch_kap_pool_q(const KapArgs& a, int dtype, int head_dim, hipStrea
 }
 
 hipError_t launch_kap_pool_k(const KapArgs& a, int dtype, int head_dim, int block, hipStream_t stream) {
-  const int64_t g2 = a.pool_last_only ? (int64_t)a.seq.batch : (int64_t)a.seq.batch * a.seq.max_nk;
+  const int64_t g2 = a.pool_last_only ? (int64_t)a.seq.batch * a.seq.h_kv : (int64_t)a.seq.batch * a.seq.max_nk;
 #define COSA_POOLK_CASE(BF, DD, BB)                                                                   \
   if ((dtype == 1) == BF && head_dim == DD && block == BB) {                                           \
     hipLaunchKernelGGL((kap_pool_k<BF, DD, BB>), dim3((unsigned)g2), dim3(kThreads), 0, stream, a); \
