@@ -19,7 +19,6 @@ import argparse
 import json
 import math
 import os
-import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -31,18 +30,20 @@ def _log(*a):
 
 
 def _timed(fn, reps, stream):
+    """Mean device time per call over `reps` back-to-back calls between one
+    pair of events (the host enqueues the next call while the device runs the
+    previous one, so per-call host work does not count as device time)."""
     import torch
     out = fn()  # warm
-    times = []
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
     for _ in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
         out = fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b))
-    return out, statistics.median(times)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return out, a.elapsed_time(b) / reps
 
 
 def main(argv=None):
