@@ -695,7 +695,6 @@ __device__ float exp32(float x) {
 
 // ---- MaxNorm, HRM, block score, flag-grouped sort, budget (R5-R10) ---------
 // One workgroup per (sequence, KV group, query block), longest rows first.
-constexpr int kMaxRankRows = 4096;  // G * (B/p) pooled rows per list
 
 // ---- proxy scores for decode problems (one pooled query row per sequence) --
 // The G query heads of a KV group are the MFMA columns (Kpool . Qpool^T with
@@ -892,10 +891,25 @@ __device__ __forceinline__ void sort_keys_desc(unsigned long long* keys, int tid
   __syncthreads();
 }
 
+// the rank pass's sort size for lists of up to max_nk blocks (a power of two,
+// at least one key per thread) and its dynamic LDS: keys, then row maxima
+__host__ __device__ inline int rank_sort_size(int max_nk) {
+  int n = kThreads;
+  while (n < max_nk) n <<= 1;
+  return n;
+}
+inline size_t rank_lds_bytes(const KapArgs& a, int block) {
+  const int nr = a.seq.group * (block / a.pool);  // G * (B/p) pooled rows per list
+  return (size_t)rank_sort_size(a.seq.max_nk) * sizeof(unsigned long long) + (size_t)nr * sizeof(float);
+}
+
 template <int BLK>
 __global__ __launch_bounds__(kThreads) void kap_rank_sort(KapArgs a) {
-  __shared__ unsigned long long keys[kMaxSortBlocks];
-  __shared__ float rmax[kMaxRankRows];
+  // keys (the sort network's size) and row maxima in LDS sized at launch
+  // (rank_lds_bytes), so short lists leave room for more workgroups per CU
+  extern __shared__ unsigned long long rank_dyn[];
+  unsigned long long* keys = rank_dyn;
+  float* rmax = (float*)(rank_dyn + rank_sort_size(a.seq.max_nk));
   const SeqArgs& sq = a.seq;
   const int G = sq.group;
   const int64_t bid = blockIdx.x;
@@ -1070,7 +1084,7 @@ hipError_t launch_all(const KapArgs& a, hipStream_t stream) {
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t g4 = (int64_t)sq.max_nq * sq.batch * sq.h_kv;
-  hipLaunchKernelGGL((kap_rank_sort<BLK>), dim3((unsigned)g4), dim3(kThreads), 0, stream, ra);
+  hipLaunchKernelGGL((kap_rank_sort<BLK>), dim3((unsigned)g4), dim3(kThreads), rank_lds_bytes(ra, BLK), stream, ra);
   return hipGetLastError();
 }
 
@@ -1109,9 +1123,9 @@ hipError_t launch_kap_pool_k(const KapArgs& a, int dtype, int head_dim, int bloc
 hipError_t launch_kap_rank(const KapArgs& a, int block, hipStream_t stream) {
   const int64_t g4 = (int64_t)a.seq.max_nq * a.seq.batch * a.seq.h_kv;
   if (block == 128)
-    hipLaunchKernelGGL((kap_rank_sort<128>), dim3((unsigned)g4), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((kap_rank_sort<128>), dim3((unsigned)g4), dim3(kThreads), rank_lds_bytes(a, 128), stream, a);
   else if (block == 64)
-    hipLaunchKernelGGL((kap_rank_sort<64>), dim3((unsigned)g4), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((kap_rank_sort<64>), dim3((unsigned)g4), dim3(kThreads), rank_lds_bytes(a, 64), stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
