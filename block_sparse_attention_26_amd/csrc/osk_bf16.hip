@@ -121,16 +121,23 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
   const SeqArgs& sq = a.seq;
   const int G = sq.group;
   // ---- unit decode: XCD-grouped, longest query block first --------------
+  // KV groups are walked in phases of kPhaseGroups; inside a phase the group
+  // index runs fastest, so every XCD shares in each group of the phase and
+  // only that phase's pages are live in the last-level cache.
   const int64_t bid = blockIdx.x;
   const int64_t xcd = bid % kNumXcd, slot = bid / kNumXcd;
   const int64_t lam = ((slot / G) * kNumXcd + xcd) * G + slot % G;
   if (lam >= a.n_units) return;
   const int hig = (int)(lam % G);
-  int64_t rest = lam / G;
-  const int g = (int)(rest % sq.h_kv);
-  rest /= sq.h_kv;
-  const int b = (int)(rest % sq.batch);
-  const int qb = sq.max_nq - 1 - (int)(rest / sq.batch);
+  const int64_t rest = lam / G;
+  const int64_t per_group = (int64_t)sq.batch * sq.max_nq;
+  const int phase = (int)(rest / ((int64_t)kPhaseGroups * per_group));
+  const int in_phase = min(kPhaseGroups, sq.h_kv - phase * kPhaseGroups);
+  const int64_t within = rest - (int64_t)phase * kPhaseGroups * per_group;
+  const int g = phase * kPhaseGroups + (int)(within % in_phase);
+  const int64_t w2 = within / in_phase;
+  const int b = (int)(w2 % sq.batch);
+  const int qb = sq.max_nq - 1 - (int)(w2 / sq.batch);
   const int h = g * G + hig;
   // sequence metadata is uniform: keep it in scalar registers
   const int q0 = __builtin_amdgcn_readfirstlane(sq.cu_seqlens_q[b]);
