@@ -91,7 +91,18 @@ __global__ __launch_bounds__(kThreads) void kap_pool_q(KapArgs a) {
   const int chunks = sq.h_q * D / 8;
   for (int c = threadIdx.x; c < chunks; c += kThreads) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int tok = lo; tok < hi; ++tok) {
+    // eight tokens' loads in flight at a time; the sum stays in token order
+    int tok = lo;
+    for (; tok + 8 <= hi; tok += 8) {
+      float x[8][8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) load8<BF16>(a.q, (size_t)(q0 + tok + u) * sq.h_q * D + (size_t)c * 8, x[u]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += x[u][i];
+    }
+    for (; tok < hi; ++tok) {
       float x[8];
       load8<BF16>(a.q, (size_t)(q0 + tok) * sq.h_q * D + (size_t)c * 8, x);
 #pragma unroll
