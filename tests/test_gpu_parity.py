@@ -9,7 +9,7 @@
 * Dense: O and lse against the fp64 dense oracle.
 Cases span several tiles, ragged tails, chunked offsets, shuffled
 NaN-poisoned page pools and packed ragged batches; GQA groups of 1, 2, 3, 4,
-8 and 16.
+8 and 16; 1, 2, 4 and 6 KV heads.
 """
 import math
 
@@ -54,6 +54,10 @@ CASES = {
     "bf16-gqa3-b64-p16": _lr("bf16-gqa3-b64-p16", 24, [1500, 400], [1500, 900], hq=6, hkv=2, d=128, B=64, p=16,
                              per_sequence_seeds=True),
     "bf16-gqa16": _lr("bf16-gqa16", 25, [900], hq=16, hkv=1, d=128, B=128, p=16),
+    # six KV groups: the attention walk's launch order takes KV groups in
+    # phases of four, so the second phase holds only two
+    "bf16-kv6-phases": _lr("bf16-kv6-phases", 26, [900, 300], [900, 700], hq=12, hkv=6, d=128, B=128, p=16,
+                           per_sequence_seeds=True),
 }
 
 
