@@ -11,8 +11,10 @@ namespace cosa {
 // its own L2); launch mappings group units that share K/V pages per XCD.
 constexpr int kNumXcd = 8;
 constexpr int kNumCu = 256;  // compute units of one MI355X
-// KV groups the attention walks at a time: at 128K tokens four groups' bf16
-// K and V (256 MB) fit the MI355X's last-level cache.
+// KV groups the attention walks at a time (its launch order): every XCD works
+// on each group of a phase instead of owning one group for the whole launch,
+// which evens the XCDs' shares; at 128K tokens four groups' bf16 K and V
+// (256 MB) also fit the MI355X's last-level cache.
 constexpr int kPhaseGroups = 4;
 
 // Largest KV-block count per sequence the proxy's in-LDS sort handles.
