@@ -23,8 +23,8 @@
 //    4k..4k+3 address 4 consecutive head-dim columns of key row K_k and every
 //    lane receives 4 keys of one column.
 //  * Per listed block: barrier A (K(t) landed, V buffer free) -> copy V(t)
-//    -> S(t) = K(t) Q^T, mask, row maxima, per-wave skip margin -> barrier C
-//    (V(t) landed, K buffer free, margins visible) -> copy K(t+1) -> unless
+//    -> S(t) = K(t) Q^T, mask, row maxima, per-wave skip vote -> barrier C
+//    (V(t) landed, K buffer free, votes visible) -> copy K(t+1) -> unless
 //    skipped, softmax and O^T += V(t)^T P(t)^T. Tiles are single-buffered
 //    (64 KB of LDS) so two workgroups share a CU: one's MFMA work overlaps the
 //    other's softmax and copy waits.
@@ -65,20 +65,6 @@ __device__ __forceinline__ float sum_xor32(float x) {
 }
 
 // max of x over lanes 0..31, valid in lane 0: within each row of 16 lanes a
-// max with a DPP-permuted copy (pair swap, quad swap, half-row mirror, row
-// mirror) leaves the row's maximum in every lane; then rows 0 and 1 combine.
-template <int CTRL>
-__device__ __forceinline__ float dpp_max(float x) {
-  return vmax(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false)));
-}
-__device__ __forceinline__ float wave_max32_lane0(float x) {
-  x = dpp_max<0xB1>(x);   // quad_perm [1,0,3,2]
-  x = dpp_max<0x4E>(x);   // quad_perm [2,3,0,1]
-  x = dpp_max<0x141>(x);  // row_half_mirror
-  x = dpp_max<0x140>(x);  // row_mirror
-  return vmax(x, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16)));
-}
-
 // max of the 16 values of an accumulator, as a shallow tree
 __device__ __forceinline__ float max16(const f32x16& v) {
   const float t0 = vmax3(v[0], v[1], v[2]), t1 = vmax3(v[3], v[4], v[5]), t2 = vmax3(v[6], v[7], v[8]);
@@ -116,7 +102,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
   constexpr int CH = Gm::CH, ROWB = Gm::ROWB, TILE = Gm::TILE, NL = Gm::NL, RPC = Gm::RPC;
   __shared__ __attribute__((aligned(1024))) unsigned char kbuf[TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char vbuf[TILE];
-  __shared__ float red[NW];
+  __shared__ uint32_t vote[NW];  // per wave: 1 when all its rows vote to skip the block
 
   const SeqArgs& sq = a.seq;
   const int G = sq.group;
@@ -399,20 +385,23 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
     m_loc = max_xor32(m_loc);
     if constexpr (!DENSE) {
       if (a.skip_on) {
-        float diff = (row_valid && m_loc != kNegInf) ? m_loc - m_run : kNegInf;
-        diff = wave_max32_lane0(diff);
-        if (lane == 0) red[w] = diff;
+        // the largest margin is below the threshold exactly when every row's
+        // is (a NaN margin never is): one ballot per wave, whose 32 rows each
+        // sit in two lanes with the same values
+        const float diff = (row_valid && m_loc != kNegInf) ? m_loc - m_run : kNegInf;
+        const bool wave_skips = __builtin_amdgcn_ballot_w64(!(diff < a.skip_thr_raw)) == 0;
+        if (lane == 0) vote[w] = wave_skips ? 1u : 0u;
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // C: V(t) landed; every wave is done with K(t); margins visible
+    __syncthreads();  // C: V(t) landed; every wave is done with K(t); votes visible
     bool skip = false;
     if constexpr (!DENSE) {
       if (a.skip_on) {
-        float worst = red[0];
+        uint32_t all = vote[0];
 #pragma unroll
-        for (int i = 1; i < NW; ++i) worst = vmax(worst, red[i]);
-        skip = __builtin_amdgcn_readfirstlane(worst < a.skip_thr_raw ? 1 : 0) != 0;
+        for (int i = 1; i < NW; ++i) all &= vote[i];
+        skip = __builtin_amdgcn_readfirstlane(all) != 0;
       }
     }
     // K(t+1): copies issued during P.V (drained before exit)
