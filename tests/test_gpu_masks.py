@@ -39,6 +39,9 @@ CASES = {
     "b64-words": _lr("b64-words", 35, [300], [9000], hq=4, hkv=2, d=64, B=64, p=16, budget=0.3,
                      sink_logit=24.0, shuffle_pages=True),
     "d128-b64": _lr("d128-b64", 36, [1300], [1400], hq=4, hkv=4, d=128, B=64, p=4),
+    # six KV heads: the walk's launch order takes KV groups in phases of four
+    "kv6-phases": _lr("kv6-phases", 37, [900, 400], [900, 1300], hq=12, hkv=6, per_sequence_seeds=True,
+                      sink_logit=24.0),
 }
 
 
