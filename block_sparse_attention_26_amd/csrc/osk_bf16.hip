@@ -379,22 +379,24 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
         for (int v = 0; v < 16; ++v)
           if (kt * 32 + 8 * (v >> 2) + (v & 3) > thr) s[kt][v] = kNegInf;
     }
-    float m_loc = max16(s[0]);
+    float m_half = max16(s[0]);  // maximum over this lane's half of the row's keys
 #pragma unroll
-    for (int kt = 1; kt < KT; ++kt) m_loc = vmax(m_loc, max16(s[kt]));
-    m_loc = max_xor32(m_loc);
+    for (int kt = 1; kt < KT; ++kt) m_half = vmax(m_half, max16(s[kt]));
     if constexpr (!DENSE) {
       if (a.skip_on) {
         // the largest margin is below the threshold exactly when every row's
-        // is (a NaN margin never is): one ballot per wave, whose 32 rows each
-        // sit in two lanes with the same values
-        const float diff = (row_valid && m_loc != kNegInf) ? m_loc - m_run : kNegInf;
+        // is, and a row's margin is exactly when both of its halves' are
+        // (subtracting the running max is monotone under rounding; a NaN
+        // margin never votes to skip): one ballot per wave over the half-row
+        // margins, before the halves are combined
+        const float diff = (row_valid && m_half != kNegInf) ? m_half - m_run : kNegInf;
         const bool wave_skips = __builtin_amdgcn_ballot_w64(!(diff < a.skip_thr_raw)) == 0;
         if (lane == 0) vote[w] = wave_skips ? 1u : 0u;
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // C: V(t) landed; every wave is done with K(t); votes visible
+    const float m_loc = max_xor32(m_half);
     bool skip = false;
     if constexpr (!DENSE) {
       if (a.skip_on) {
