@@ -242,7 +242,7 @@ __global__ __launch_bounds__(2 * BLK, 1) void osk_kernel(OskArgs a) {  // 2*BLK 
     n_list = n_causal;
   } else {
     const int64_t list_row = ((int64_t)b * sq.h_kv + g) * sq.max_nq + qb;
-    n_list = min(a.count[list_row], a.kmax);  // a corrupt count cannot overrun the row
+    n_list = max(0, min(a.count[list_row], a.kmax));  // a corrupt count can neither overrun nor underrun the row
     lst = a.order + list_row * a.kmax;
   }
   const int64_t out_row = ((int64_t)b * sq.h_q + h) * sq.max_nq + qb;

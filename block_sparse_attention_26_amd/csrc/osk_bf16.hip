@@ -172,7 +172,8 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
     n_list = n_causal;
     if constexpr (MASK) mrow = a.mask + list_row * a.mask_words;
   } else {
-    n_list = min(__builtin_amdgcn_readfirstlane(a.count[list_row]), a.kmax);  // a corrupt count cannot overrun the row
+    // clamped to [0, kmax]: a corrupt count can neither overrun nor underrun the row
+    n_list = max(0, min(__builtin_amdgcn_readfirstlane(a.count[list_row]), a.kmax));
     lst = a.order + list_row * a.kmax;
   }
   int bad = 0;

@@ -165,6 +165,16 @@ def test_empty_and_corrupt_lists(run):
     order[0, 0, 0, :] = 1 << 30
     count[0, g_last, last_qb] = 0
     order[0, g_last, last_qb, :] = -5
+    # a negative count reads as an empty list (no entry read, nothing written
+    # before the row's own skip bits)
+    empty = [(0, 0), (g_last, last_qb)]
+    if case.h_kv > 1 and last_qb >= 1:
+        empty.append((g_last, 0))
+    elif last_qb >= 2:
+        empty.append((0, 1))
+    if len(empty) == 3:
+        count[0, empty[2][0], empty[2][1]] = -1000
+        order[0, empty[2][0], empty[2][1], :] = 1 << 29
     # a corrupt row (needs a second query block and a list of two entries)
     corrupt = last_qb >= 1 and count[0, 0, last_qb] >= 2
     if corrupt:  # the first block past the row's causal range
@@ -181,7 +191,7 @@ def test_empty_and_corrupt_lists(run):
     O0 = base["O"].float().cpu().numpy()
     lse, lse0 = g["lse"].cpu().numpy(), base["lse"].cpu().numpy()
     touched = np.zeros(O.shape[:2], dtype=bool)  # [token, head]
-    for (gg, qb) in ((0, 0), (g_last, last_qb)):
+    for (gg, qb) in empty:
         rows = slice(qb * B, min(qb * B + B, lq0))
         heads = slice(gg * grp, (gg + 1) * grp)
         assert np.all(O[rows, heads] == 0.0)
@@ -199,3 +209,12 @@ def test_empty_and_corrupt_lists(run):
     keep = ~touched
     assert np.array_equal(O[keep].view(np.uint32), O0[keep].view(np.uint32))
     assert np.array_equal(lse.T[keep].view(np.uint32), lse0.T[keep].view(np.uint32))
+    # per-row counters and skip bits of every other row are those of the clean run
+    row_keep = np.ones(g["visited"].shape, dtype=bool)  # [b, h_q, nq]
+    for (gg, qb) in empty:
+        row_keep[0, gg * grp:(gg + 1) * grp, qb] = False
+    if corrupt:
+        row_keep[0, 0:grp, last_qb] = False
+    for name in ("visited", "skipped", "skip_bits"):
+        a_, b_ = g[name].cpu().numpy(), base[name].cpu().numpy()
+        assert np.array_equal(a_[row_keep], b_[row_keep]), name
