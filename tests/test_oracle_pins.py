@@ -424,3 +424,118 @@ def test_generator_determinism():
     for pg in range(c.k_pages.shape[0]):
         if pg not in used:
             assert torch.isnan(c.k_pages[pg].float()).all()
+
+
+# ------------------------------------------- hand pins: paging, R4, R7, R9 ---
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_gather_pages_hand_example():
+    """Logical KV blocks come from the pages the block table names, in table
+    order (KV-head-major pages, CompactAttention page, execution stage)."""
+    ex_ = _load("gather_pages_hand_example.json")
+    P, H, B = ex_["num_pages"], ex_["h_kv"], ex_["block"]
+    pages = np.zeros((P, H, B, 1))
+    for p_ in range(P):
+        for h in range(H):
+            for r in range(B):
+                pages[p_, h, r, 0] = 100 * p_ + 10 * h + r
+    got = layout.gather_pages(pages, np.array(ex_["table_row"], dtype=np.int32), ex_["seqlen_k"])
+    assert got.shape == (ex_["seqlen_k"], H, 1)
+    assert got[:, 0, 0].tolist() == ex_["expected"]["head0"]
+    assert got[:, 1, 0].tolist() == ex_["expected"]["head1"]
+
+
+def test_shuffled_pages_give_the_same_oracle_results():
+    """The page pool's arrangement is not part of the method: the same logical
+    K/V in a shuffled, NaN-padded pool gives the same proxy lists and the same
+    attention output as in an identity-ordered pool."""
+    kw = dict(h_q=4, h_kv=2, head_dim=16, block=64, pool=8, budget=0.3, dtype="f32")
+    a = synthetic.lowrank_case(31, [300], [700], **kw)
+    b = synthetic.lowrank_case(31, [300], [700], shuffle_pages=True, spare_pages=3, **kw)
+    assert not np.array_equal(a.block_table.numpy(), b.block_table.numpy())
+    ka, kb_ = cases.kap_case(a), cases.kap_case(b)
+    for name in ("order", "hrm", "count"):
+        np.testing.assert_array_equal(ka[name], kb_[name])
+    oa = cases.osk_case(a, ka["order"], ka["count"])
+    ob = cases.osk_case(b, ka["order"], ka["count"])
+    assert np.isfinite(ob["O"]).all()
+    np.testing.assert_array_equal(oa["O"], ob["O"])
+    np.testing.assert_array_equal(cases.dense_case(a)["O"], cases.dense_case(b)["O"])
+
+
+@pytest.mark.parametrize("precision", ["fp64", "fp32"])
+def test_kap_chunk_offset_not_multiple_of_pool(precision):
+    """R4 at a chunked offset (7) that the pool factor (2) does not divide: the
+    last token of a pooled query window decides which pooled keys it sees."""
+    ex_ = _load("kap_chunk_offset_hand_example.json")
+    pr = ex_["params"]
+    q = np.array(ex_["q"], dtype=np.float64)[:, None, None]
+    k = np.array(ex_["k"], dtype=np.float64)[:, None, None]
+    out = kap.kap_sequence(q, k, pr["scale"], pr["block"], pr["pool"], 1.0, 3, precision)
+    assert out["P"][0].tolist() == ex_["expected"]["P"]
+    for qb in range(2):
+        assert out["count"][0, qb] == 3
+        assert out["order"][0, qb].tolist() == ex_["expected"]["order"][qb]
+        assert out["hrm"][0, qb].tolist() == ex_["expected"]["hrm"][qb]
+    assert np.allclose(out["s"][0, 0], ex_["expected"]["s_qb0"], rtol=0, atol=1e-7)
+    assert np.allclose(out["s"][0, 1], ex_["expected"]["s_qb1"], rtol=0, atol=1e-7)
+
+
+@pytest.mark.parametrize("precision", ["fp64", "fp32"])
+def test_kap_tie_break_order(precision):
+    """R9: equal block scores are ordered by ascending KV block index, inside
+    the HRM group and inside the rest, and the budget cut respects it."""
+    ex_ = _load("kap_tie_break_hand_example.json")
+    pr = ex_["params"]
+    q = np.array(ex_["q"], dtype=np.float64)[:, None, None]
+    k = np.array(ex_["k"], dtype=np.float64)[:, None, None]
+    for budget, want in ex_["expected"].items():
+        kmax = len(want["qb3"])
+        out = kap.kap_sequence(q, k, pr["scale"], pr["block"], pr["pool"], float(budget), kmax, precision)
+        assert out["s"][0, 3, 1] == out["s"][0, 3, 2]  # an exact tie
+        assert out["order"][0, 3].tolist() == want["qb3"]
+        assert out["hrm"][0, 3].tolist() == want["qb3_hrm"]
+        if "qb2" in want:
+            assert out["order"][0, 2, :3].tolist() == want["qb2"]
+            assert out["hrm"][0, 2, :3].tolist() == want["qb2_hrm"]
+
+
+def _sum_order_P(ex_, part):
+    d24 = np.array([int(ex_["D24_bits"], 16)], dtype=np.uint32).view(np.float32)[0]
+    tok = {"0": np.float32(0.0), "-100": np.float32(-100.0), "-inf": np.float32(-np.inf), "D24": d24}
+    return np.array([[[tok[x] for x in row] for row in head] for head in part["P"]], dtype=np.float32)
+
+
+def test_kap_sum_order_bits():
+    """R7: the block score is a sequential fp32 sum, heads outer and pooled
+    rows inner, each add rounded to nearest even; three blocks whose bits each
+    expose a different summation order."""
+    ex_ = _load("kap_sum_order_hand_example.json")
+    pr = ex_["params"]
+    P = _sum_order_P(ex_, ex_)
+    assert ex32(np.float32(P[0, 2, 0])) == np.float32(2.0 ** -24)
+    out = kap.kap_from_scores(P, pr["h_q"] // pr["h_kv"], pr["block"], pr["pool"], pr["Lq"], pr["Lk"],
+                              pr["budget"], 3, "fp32")
+    bits = lambda x: [f"0x{int(v):08x}" for v in np.asarray(x, dtype=np.float32).view(np.uint32)]
+    assert bits(out["s"][0, 1]) == ex_["expected"]["s_qb1_bits"]
+    assert bits(out["s"][0, 0]) == ex_["expected"]["s_qb0_bits"]
+    assert out["order"][0].tolist() == ex_["expected"]["order"]
+    assert out["hrm"][0].tolist() == ex_["expected"]["hrm"]
+    assert out["count"][0].tolist() == ex_["expected"]["count"]
+    # eight terms per block: pairwise and blocked sums differ from the sequential one
+    pb = ex_["part_b"]
+    prb = pb["params"]
+    out = kap.kap_from_scores(_sum_order_P(ex_, pb), prb["h_q"] // prb["h_kv"], prb["block"], prb["pool"],
+                              prb["Lq"], prb["Lk"], prb["budget"], 2, "fp32")
+    assert bits(out["s"][0, 0]) == pb["expected"]["s_bits"]
+    assert out["order"][0, 0].tolist() == pb["expected"]["order"]
+    assert out["hrm"][0, 0].tolist() == pb["expected"]["hrm"]
+    assert out["count"][0, 0] == pb["expected"]["count"]
+
+
+def ex32(x):
+    return ex.exp32(np.asarray([x], dtype=np.float32))[0]
