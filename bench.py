@@ -57,7 +57,58 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (HBM counter calibration)")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="only time large bf16 matrix products (torch.matmul, the vendor GEMM): the "
+                         "MFMA rate the box sustains, against which the walk's fraction of peak is read")
     return ap.parse_args()
+
+
+def blas_info():
+    """Vendor, version and thread count of the BLAS numpy calls into."""
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return {"vendor": i.get("internal_api"), "version": i.get("version"),
+                        "threads": i.get("num_threads"), "library": os.path.basename(i.get("filepath", ""))}
+    except Exception:
+        pass
+    return {"vendor": "unknown", "version": None, "threads": os.cpu_count() or 1, "library": ""}
+
+
+def gemm_ceiling(sizes=((8192, 8192, 8192), (16384, 16384, 16384)), reps=20):
+    """bf16 C = A.B with torch.matmul (hipBLASLt on ROCm) at large square sizes:
+    TFLOP/s from HIP events around `reps` back-to-back products after a warm-up."""
+    import torch
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    out = []
+    for (m, n, k) in sizes:
+        g = torch.Generator(device="cpu").manual_seed(5)
+        a = torch.randn((m, k), generator=g).to(dev, torch.bfloat16)
+        b = torch.randn((k, n), generator=g).to(dev, torch.bfloat16)
+        c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ms = []
+        for _ in range(reps):
+            e0.record(stream)
+            torch.matmul(a, b, out=c)
+            e1.record(stream)
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        ms.sort()
+        med = ms[len(ms) // 2]
+        fl = 2.0 * m * n * k
+        out.append({"m": m, "n": n, "k": k, "median_ms": med, "min_ms": ms[0],
+                    "tflops_median": fl / (med * 1e-3) / 1e12, "tflops_best": fl / (ms[0] * 1e-3) / 1e12})
+        print(f"[gemm] {m}x{n}x{k} bf16: median {med:.3f} ms = {out[-1]['tflops_median']:.0f} TFLOP/s "
+              f"(best {out[-1]['tflops_best']:.0f})", file=sys.stderr, flush=True)
+        del a, b, c
+    print(json.dumps({"gemm_ceiling": out, "peak_bf16_tflops": MFMA_BF16_PEAK_TFLOPS}), flush=True)
 
 
 OSK_SOURCE = os.path.join(ROOT, "block_sparse_attention_26_amd", "csrc", "osk_bf16.hip")
@@ -89,11 +140,8 @@ def cpu_baseline(case, kap_count, seconds_target=20.0):
     import numpy as np
     from oracle import kap as okap, osk as oosk, layout
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    blas = blas_info()
+    cores = int(blas["threads"] or 1)
     G = case.h_q // case.h_kv
     B, p = case.block, case.pool
     T = case.seqlens_q[0]
@@ -123,6 +171,7 @@ def cpu_baseline(case, kap_count, seconds_target=20.0):
     return {
         "layer_seconds": layer_s,
         "cores": int(cores),
+        "blas": blas,
         "sample": (f"oracle (numpy fp64) proxy of KV group 0 over all {T} tokens ({t_kap:.1f} s, x{case.h_kv} groups) "
                    f"+ ordered walk of KV group 0 ({G} query heads) over {len(done_q)} query blocks "
                    f"({done_blocks} listed blocks, {t_osk:.1f} s), extrapolated by listed-block count "
@@ -139,12 +188,15 @@ def main():
     import numpy as np
     import torch
 
-    import block_sparse_attention_26_amd as cosa
-    import synthetic
-
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.gemm_ceiling:
+        gemm_ceiling()
+        return
+
+    import block_sparse_attention_26_amd as cosa
+    import synthetic
     cfg_n, default_budget, desc = WORKLOADS[args.workload]
     budget = default_budget if args.budget is None else args.budget
     kw = {}
@@ -212,6 +264,9 @@ def main():
     ms_step = t_start.elapsed_time(t_end) / K
     kap_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
     osk_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    step_ms = sorted(e[0].elapsed_time(e[2]) for e in ev)
+    osk_sorted = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    med = lambda xs: xs[len(xs) // 2] if len(xs) % 2 else 0.5 * (xs[len(xs) // 2 - 1] + xs[len(xs) // 2])
     print(f"[bench] timed {K} steps: {ms_step:.3f} ms/step (kap {kap_ms:.3f}, osk {osk_ms:.3f})",
           file=sys.stderr, flush=True)
 
@@ -287,8 +342,12 @@ def main():
             "budget": case.budget, "skip_threshold": case.tau,
         },
         "ms_per_layer": ms_step,
+        "ms_per_layer_median": med(step_ms),
+        "ms_per_layer_min": step_ms[0],
         "kap_ms": kap_ms,
         "osk_ms": osk_ms,
+        "osk_ms_median": med(osk_sorted),
+        "osk_ms_min": osk_sorted[0],
         "dense_ms": dense_ms,
         "speedup_vs_dense": (dense_ms / ms_step) if dense_ms else None,
         "dense_tflops": (dense_flops / (dense_ms * 1e-3) / 1e12) if dense_ms else None,
