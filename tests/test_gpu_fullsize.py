@@ -1,87 +1,63 @@
-"""Full-size parity at the 128K-token, 10%-budget layer (32 query / 8 KV heads,
-head_dim 128, bf16, block 128, pool 16, 32 needle blocks per KV head), in the
-launch configuration the benchmark times (proxy in workspace mode, ordered
-walk without diagnostics), checked on sampled outputs the oracle computes one
-by one: list rows of two KV groups at several query blocks, and the output
-rows of those query blocks."""
+"""Full-size parity at the 128K-token prefill (32 query / 8 KV heads, head_dim
+128, bf16, block 128, pool 16, 32 needle blocks per KV head) at budgets 5%,
+10% and 25%, and at 10% with aligned sink keys (the case in which tiles are
+skipped in-kernel), in the launch configuration the benchmark times (proxy in
+workspace mode, ordered walk without diagnostics) plus a diagnostic run that
+must agree with it bit for bit.
+
+Checked on outputs the oracle computes one by one: list rows (all of them at
+10%, every fourth query block and the last two otherwise) bit-exact against
+the oracle fed the GPU's proxy scores; the output and skip sets of four KV
+groups at sixteen query blocks (first two, last two, twelve evenly spaced)
+against the oracle's ordered walk; at 10% also the dense kernel on sampled
+query blocks; per-layer list totals against their closed forms.
+"""
 import numpy as np
 import pytest
-import torch
 
-import block_sparse_attention_26_amd as cosa
 import synthetic
-from oracle import dense as odense, kap as okap, layout, osk as oosk
-from gpu_common import AMBIGUOUS_NATS, TOL, require_gpu, say
+from oracle import layout
+from gpu_common import check_dense, check_lists, check_walk, require_gpu, run_gpu, sample_qbs, say
 
 pytestmark = pytest.mark.gpu
 
-GROUPS = (0, 7)
-QBS = (0, 1, 100, 511, 1022, 1023)
+# name: (budget, aligned-sink logit or None, listed blocks per KV head in closed form)
+VARIANTS = {
+    "b10": (0.10, None, 52942),
+    "b05": (0.05, None, 26728),
+    "b25": (0.25, None, 131584),
+    "b10-sinks": (0.10, 24.0, 52942),
+}
+GROUPS = (0, 3, 4, 7)  # both phases of the walk's four-group launch order
 
 
-def test_full_128k_sampled():
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_full_128k(variant):
     require_gpu()
-    case = synthetic.config_case(3)
-    say("128K case generated", tuple(case.q.shape))
-    q, k, v = case.q.cuda(), case.k_pages.cuda(), case.v_pages.cuda()
-    pr = cosa.Problem.from_case(case)
-    G = case.h_q // case.h_kv
-    B, p = case.block, case.pool
-    T = case.seqlens_q[0]
+    budget, sink, per_head = VARIANTS[variant]
+    kw = {} if sink is None else {"sink_logit": sink}
+    case = synthetic.config_case(3, budget=budget, **kw)
+    case.name = f"128K-{variant}"
+    say(case.name, "generated", tuple(case.q.shape))
+    g = run_gpu(case)
+    nq = layout.cdiv(case.seqlens_q[0], case.block)
+    assert int(g["count"].sum()) == per_head * case.h_kv
+    rows = None if variant == "b10" else [sorted(set(range(0, nq, 4)) | {nq - 2, nq - 1})]
+    say(case.name, "lists")
+    check_lists(case, g, budget, rows=rows)
+    qbs = sample_qbs(nq, 12)
+    say(case.name, "walk of four KV groups at the sampled query blocks")
+    mx, mean, n_amb, n_skip = _walk_groups(case, g, qbs)
+    say(case.name, f"walk: max err {mx:.3e} mean {mean:.3e}, {n_skip} skipped, {n_amb} ambiguous")
+    if sink is not None:
+        assert n_skip > 0, "aligned sinks must make the walk skip tiles"
+    if variant == "b10":
+        say(case.name, "dense on sampled query blocks")
+        check_dense(case, g["dev"], [[0, 1, nq // 2, nq - 1]])
 
-    say("128K kap (workspace mode)")
-    ka = cosa.kap_order(pr, q, k, p, case.budget)
-    say("128K osk (timed configuration)")
-    oa = cosa.osk_attention(pr, q, k, v, ka["order"], ka["count"], case.tau)
-    say("128K kap (export) + osk (diagnostics)")
-    kx = cosa.kap_order(pr, q, k, p, case.budget, export_scores=True, export_block_scores=True)
-    ox = cosa.osk_attention(pr, q, k, v, ka["order"], ka["count"], case.tau, skip_bits=True)
-    say("128K dense")
-    de = cosa.dense_attention(pr, q, k, v)
-    torch.cuda.synchronize()
 
-    for name in ("order", "hrm", "count"):
-        assert torch.equal(ka[name], kx[name]), name
-    assert torch.equal(oa["O"].view(torch.int16), ox["O"].view(torch.int16))
-    assert int(ka["count"].sum()) == 52942 * case.h_kv  # closed form at 10%
-
-    order = ka["order"].cpu().numpy()[0]
-    count = ka["count"].cpu().numpy()[0]
-    hrm = ka["hrm"].cpu().numpy()[0]
-    s_gpu = kx["s"][0].cpu().numpy()
-    for g in GROUPS:
-        for qb in QBS:
-            n = layout.n_causal_blocks(qb, B, T, T)
-            rows = kx["P"][0, g * G : (g + 1) * G, qb * (B // p) : (qb + 1) * (B // p), :n].cpu().numpy()
-            s, fl = okap.rank_row(rows, "fp32")
-            lst, flags = okap.select_row(s, fl, n, case.budget)
-            assert count[g, qb] == len(lst)
-            assert order[g, qb, : len(lst)].tolist() == lst, (g, qb)
-            assert hrm[g, qb, : len(lst)].tolist() == flags, (g, qb)
-            assert np.array_equal(s_gpu[g, qb, :n].view(np.uint32), s.view(np.uint32)), (g, qb)
-
-    bits = ox["skip_bits"][0].cpu().numpy()
-    O = oa["O"]
-    Od = de["O"]
-    mx, mean = TOL["bf16"]
-    for g in GROUPS:
-        hs = slice(g * G, (g + 1) * G)
-        qg = case.q[:, hs].float().numpy()
-        kg = case.kv_contiguous(0, "k")[:, g : g + 1].float().numpy()
-        vg = case.kv_contiguous(0, "v")[:, g : g + 1].float().numpy()
-        say("oracle group", g)
-        ref = oosk.osk_sequence(qg, kg, vg, order[g : g + 1], count[g : g + 1], case.scale, case.tau, G, B,
-                                query_blocks=list(QBS))
-        rows = np.concatenate([np.arange(qb * B, qb * B + B) for qb in QBS])
-        got = O[rows][:, hs].float().cpu().numpy()
-        err = np.abs(got - ref["O"][rows])
-        assert err.max() <= mx and err.mean() <= mean, (g, err.max(), err.mean())
-        amb = np.abs(ref["margin"]) < AMBIGUOUS_NATS
-        for qb in QBS:
-            c = count[g, qb]
-            gb = bits[hs, qb, :c]
-            rb = ref["skip_bits"][:, qb, :c]
-            assert not ((gb != rb) & ~amb[:, qb, :c]).any(), (g, qb)
-        dref, _ = odense.dense_sequence(qg, kg, vg, case.scale, rows=rows, row_chunk=128)
-        derr = np.abs(Od[rows][:, hs].float().cpu().numpy() - dref)
-        assert derr.max() <= mx and derr.mean() <= mean, (g, derr.max(), derr.mean())
+def _walk_groups(case, g, qbs):
+    """check_walk restricted to GROUPS (the oracle's walk is per KV group)."""
+    import gpu_common as gc
+    return gc.check_walk(case, g, [qbs], groups=GROUPS)
