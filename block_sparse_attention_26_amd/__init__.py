@@ -32,7 +32,7 @@ __all__ = [
     "cosa_last_error", "cosa_version", "cosa_mask_from_order", "cosa_order_from_mask",
     "cosa_osk_attention_masked", "cosa_block_mass", "cosa_union_order",
     "cosa_osk_decode", "cosa_osk_decode_workspace_size", "cosa_kap_rank", "cosa_cobs_scores",
-    "cosa_cobs_workspace_size", "cosa_kap_pool_keys", "cosa_kap_order_pooled",
+    "cosa_cobs_workspace_size", "cosa_kap_pool_keys", "cosa_kap_order_pooled", "cosa_kap_kmax",
     "kap_order", "pool_keys", "osk_attention", "dense_attention", "mask_from_order", "order_from_mask",
     "osk_attention_masked", "mask_words_for", "block_mass", "union_order", "osk_decode", "kap_rank",
     "cobs_scores",
@@ -50,7 +50,7 @@ EXPORTED_SYMBOLS = (
     "cosa_last_error", "cosa_version", "cosa_mask_from_order", "cosa_order_from_mask",
     "cosa_osk_attention_masked", "cosa_block_mass", "cosa_union_order",
     "cosa_osk_decode", "cosa_osk_decode_workspace_size", "cosa_kap_rank", "cosa_cobs_scores",
-    "cosa_cobs_workspace_size", "cosa_kap_pool_keys", "cosa_kap_order_pooled",
+    "cosa_cobs_workspace_size", "cosa_kap_pool_keys", "cosa_kap_order_pooled", "cosa_kap_kmax",
 )
 
 
@@ -69,6 +69,8 @@ class cosa_problem(ctypes.Structure):
         ("cu_seqlens_q", ctypes.c_void_p), ("seqlens_k", ctypes.c_void_p),
         ("block_table", ctypes.c_void_p),
         ("host_cu_seqlens_q", ctypes.c_void_p), ("host_seqlens_k", ctypes.c_void_p),
+        ("q_stride_tok", ctypes.c_int64), ("q_stride_head", ctypes.c_int64),
+        ("o_stride_tok", ctypes.c_int64), ("o_stride_head", ctypes.c_int64),
     ]
 
 
@@ -99,6 +101,7 @@ def load():
         "cosa_validate": (i32, [P]),
         "cosa_dims": (i32, [P, i32, f64, ctypes.POINTER(cosa_dims_t)]),
         "cosa_kap_workspace_size": (sz, [P, i32, i32]),
+        "cosa_kap_kmax": (sz, [P, f64]),
         "cosa_kap_order": (i32, [P, vp, vp, i32, f64, vp, vp, vp, i32, vp, vp, vp, sz, vp]),
         "cosa_osk_attention": (i32, [P, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp, vp, vp, vp, vp]),
         "cosa_dense_attention": (i32, [P, vp, vp, vp, vp, vp, vp]),
@@ -154,6 +157,10 @@ def cosa_dims(problem: "cosa_problem", pool: int, budget: float) -> "cosa_dims_t
     d = cosa_dims_t()
     _check(load().cosa_dims(ctypes.byref(problem), int(pool), float(budget), ctypes.byref(d)))
     return d
+
+
+def cosa_kap_kmax(problem: "cosa_problem", budget: float) -> int:
+    return load().cosa_kap_kmax(ctypes.byref(problem), float(budget))
 
 
 def cosa_kap_workspace_size(problem: "cosa_problem", pool: int, with_scores: bool) -> int:
@@ -247,6 +254,21 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _need(t, name, *, shape=None, dtype=None, device=None, contiguous=True):
+    """Raise ValueError unless tensor t matches what the library will assume."""
+    if t is None:
+        raise ValueError(f"{name} is None")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         import torch
@@ -280,6 +302,58 @@ class Problem:
         )
         self.group = h_q // h_kv
 
+    # -- tensor checks (shapes and dtypes the C ABI assumes) --------------------
+    def torch_dtype(self):
+        import torch
+        return torch.bfloat16 if self.c.dtype == COSA_BF16 else torch.float32
+
+    def _rows_view(self, t, name):
+        """q or o: a [total_q, h_q, head_dim] view whose head_dim is contiguous
+        (token and head strides are passed to the library)."""
+        c = self.c
+        _need(t, name, shape=(self.dims().total_q, c.h_q, c.head_dim), dtype=self.torch_dtype(),
+              contiguous=False)
+        if t.stride(2) != 1:
+            raise ValueError(f"{name} must have a contiguous head_dim (stride {t.stride(2)})")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        return t
+
+    def check_pages(self, k_pages, name="k_pages"):
+        c = self.c
+        _need(k_pages, name, shape=(c.num_pages, c.h_kv, c.block, c.head_dim), dtype=self.torch_dtype())
+        if not k_pages.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        return k_pages
+
+    def check_lists(self, order, count, device=None):
+        import torch
+        c = self.c
+        d = self.dims()
+        if order.dim() != 4:
+            raise ValueError(f"order must be [batch, h_kv, max_nq, kmax], got shape {tuple(order.shape)}")
+        _need(order, "order", shape=(c.batch, c.h_kv, d.max_nq, order.shape[3]), dtype=torch.int32,
+              device=device)
+        _need(count, "count", shape=(c.batch, c.h_kv, d.max_nq), dtype=torch.int32, device=device)
+        return int(order.shape[3])
+
+    def for_tensors(self, q, o=None) -> "cosa_problem":
+        """A copy of the problem struct carrying q's (and o's) element strides."""
+        c = cosa_problem.from_buffer_copy(self.c)
+        self._rows_view(q, "q")
+        c.q_stride_tok, c.q_stride_head = q.stride(0), q.stride(1)
+        if o is not None:
+            self._rows_view(o, "o")
+            if o.device != q.device:
+                raise ValueError("o and q must be on the same device")
+            c.o_stride_tok, c.o_stride_head = o.stride(0), o.stride(1)
+        return c
+
+    def new_rows(self, q):
+        """A contiguous output tensor shaped like q."""
+        import torch
+        return torch.empty(tuple(q.shape), dtype=q.dtype, device=q.device)
+
     @classmethod
     def from_case(cls, case, device="cuda"):
         """Build from a ``synthetic.Case``, copying its metadata to the device."""
@@ -302,9 +376,12 @@ def pool_keys(problem: Problem, k_pages, pool: int, *, out=None, last_block_only
     """Pooled keys [num_pages, h_kv, B/p, d] (into ``out`` when given)."""
     import torch
     c = problem.c
+    problem.check_pages(k_pages)
     if out is None:
         out = torch.zeros((c.num_pages, c.h_kv, c.block // pool, c.head_dim), dtype=k_pages.dtype,
                           device=k_pages.device)
+    _need(out, "out", shape=(c.num_pages, c.h_kv, c.block // pool, c.head_dim), dtype=k_pages.dtype,
+          device=k_pages.device)
     cosa_kap_pool_keys(c, k_pages.data_ptr(), pool, out.data_ptr(), last_block_only, _stream(stream))
     return out
 
@@ -316,6 +393,9 @@ def kap_order(problem: Problem, q, k_pages, pool: int, budget: float, *, kmax=No
     ``pooled_keys`` (from ``pool_keys``) the keys are not pooled again."""
     import torch
     dev = q.device
+    c = problem.for_tensors(q)
+    if pooled_keys is None:
+        problem.check_pages(k_pages)
     d = problem.dims(pool, budget)
     kmax = d.kmax if kmax is None else int(kmax)
     order = torch.empty((problem.c.batch, problem.c.h_kv, d.max_nq, kmax), dtype=torch.int32, device=dev)
@@ -329,11 +409,14 @@ def kap_order(problem: Problem, q, k_pages, pool: int, budget: float, *, kmax=No
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     if pooled_keys is None:
-        cosa_kap_order(problem.c, q.data_ptr(), k_pages.data_ptr(), pool, budget, order.data_ptr(),
+        cosa_kap_order(c, q.data_ptr(), k_pages.data_ptr(), pool, budget, order.data_ptr(),
                        hrm.data_ptr(), count.data_ptr(), kmax, _ptr(P), _ptr(s), workspace.data_ptr(),
                        workspace.numel(), _stream(stream))
     else:
-        cosa_kap_order_pooled(problem.c, q.data_ptr(), pooled_keys.data_ptr(), pool, budget, order.data_ptr(),
+        pc = problem.c
+        _need(pooled_keys, "pooled_keys", shape=(pc.num_pages, pc.h_kv, pc.block // pool, pc.head_dim),
+              dtype=problem.torch_dtype(), device=dev)
+        cosa_kap_order_pooled(c, q.data_ptr(), pooled_keys.data_ptr(), pool, budget, order.data_ptr(),
                               hrm.data_ptr(), count.data_ptr(), kmax, _ptr(P), _ptr(s), workspace.data_ptr(),
                               workspace.numel(), _stream(stream))
     out = {"order": order, "hrm": hrm, "count": count, "kmax": kmax, "workspace": workspace}
@@ -350,14 +433,17 @@ def osk_attention(problem: Problem, q, k_pages, v_pages, order, count, tau: floa
     import torch
     dev = q.device
     d = problem.dims()
-    kmax = int(order.shape[3])
-    o = torch.empty_like(q) if out is None else out
+    problem.check_pages(k_pages)
+    problem.check_pages(v_pages, "v_pages")
+    kmax = problem.check_lists(order, count, dev)
+    o = problem.new_rows(q) if out is None else out
+    c = problem.for_tensors(q, o)
     vis = torch.empty((problem.c.batch, problem.c.h_q, d.max_nq), dtype=torch.int32, device=dev)
     skp = torch.empty_like(vis)
     bits = (torch.empty((problem.c.batch, problem.c.h_q, d.max_nq, kmax), dtype=torch.uint8, device=dev)
             if skip_bits else None)
     ls = torch.empty((problem.c.h_q, d.total_q), dtype=torch.float32, device=dev) if lse else None
-    cosa_osk_attention(problem.c, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+    cosa_osk_attention(c, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
                        order.data_ptr(), count.data_ptr(), kmax, problem.group, tau, o.data_ptr(),
                        vis.data_ptr(), skp.data_ptr(), _ptr(bits), _ptr(ls), _stream(stream))
     res = {"O": o, "visited": vis, "skipped": skp}
@@ -373,9 +459,12 @@ def dense_attention(problem: Problem, q, k_pages, v_pages, *, lse: bool = False,
     """Dense causal attention; returns dict(O[, lse])."""
     import torch
     d = problem.dims()
-    o = torch.empty_like(q) if out is None else out
+    problem.check_pages(k_pages)
+    problem.check_pages(v_pages, "v_pages")
+    o = problem.new_rows(q) if out is None else out
+    c = problem.for_tensors(q, o)
     ls = torch.empty((problem.c.h_q, d.total_q), dtype=torch.float32, device=q.device) if lse else None
-    cosa_dense_attention(problem.c, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+    cosa_dense_attention(c, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
                          o.data_ptr(), _ptr(ls), _stream(stream))
     res = {"O": o}
     if ls is not None:
@@ -391,6 +480,7 @@ def mask_from_order(problem: Problem, order, count, *, mask_words=None, stream=N
     """Binary block mask (int64 view of the uint64 words) of the listed blocks."""
     import torch
     d = problem.dims()
+    problem.check_lists(order, count, order.device)
     mw = mask_words_for(problem) if mask_words is None else int(mask_words)
     mask = torch.empty((problem.c.batch, problem.c.h_kv, d.max_nq, mw), dtype=torch.int64, device=order.device)
     cosa_mask_from_order(problem.c, order.data_ptr(), count.data_ptr(), int(order.shape[3]),
@@ -404,6 +494,10 @@ def order_from_mask(problem: Problem, mask, kmax: int, *, device=None, stream=No
     import torch
     d = problem.dims()
     dev = mask.device if mask is not None else device
+    if mask is not None:
+        if mask.dim() != 4:
+            raise ValueError(f"mask must be [batch, h_kv, max_nq, mask_words], got shape {tuple(mask.shape)}")
+        _need(mask, "mask", shape=(problem.c.batch, problem.c.h_kv, d.max_nq, mask.shape[3]), dtype=torch.int64)
     order = torch.empty((problem.c.batch, problem.c.h_kv, d.max_nq, int(kmax)), dtype=torch.int32, device=dev)
     count = torch.empty(order.shape[:3], dtype=torch.int32, device=dev)
     mw = int(mask.shape[3]) if mask is not None else 0
@@ -418,11 +512,18 @@ def osk_attention_masked(problem: Problem, q, k_pages, v_pages, mask, tau: float
     import torch
     dev = q.device
     d = problem.dims()
-    o = torch.empty_like(q) if out is None else out
+    problem.check_pages(k_pages)
+    problem.check_pages(v_pages, "v_pages")
+    if mask.dim() != 4:
+        raise ValueError(f"mask must be [batch, h_kv, max_nq, mask_words], got shape {tuple(mask.shape)}")
+    _need(mask, "mask", shape=(problem.c.batch, problem.c.h_kv, d.max_nq, mask.shape[3]), dtype=torch.int64,
+          device=dev)
+    o = problem.new_rows(q) if out is None else out
+    c = problem.for_tensors(q, o)
     vis = torch.empty((problem.c.batch, problem.c.h_q, d.max_nq), dtype=torch.int32, device=dev)
     skp = torch.empty_like(vis)
     ls = torch.empty((problem.c.h_q, d.total_q), dtype=torch.float32, device=dev) if lse else None
-    cosa_osk_attention_masked(problem.c, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+    cosa_osk_attention_masked(c, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
                               mask.data_ptr(), int(mask.shape[3]), problem.group, tau, o.data_ptr(),
                               vis.data_ptr(), skp.data_ptr(), _ptr(ls), _stream(stream))
     res = {"O": o, "visited": vis, "skipped": skp}
@@ -437,6 +538,7 @@ def kap_rank(problem: Problem, scores, pool: int, budget: float, *, kmax=None, e
     import torch
     dev = scores.device
     d = problem.dims(pool, budget)
+    _need(scores, "scores", shape=(problem.c.batch, problem.c.h_q, d.max_nr, d.max_nk), dtype=torch.float32)
     kmax = d.kmax if kmax is None else int(kmax)
     order = torch.empty((problem.c.batch, problem.c.h_kv, d.max_nq, kmax), dtype=torch.int32, device=dev)
     hrm = torch.empty(order.shape, dtype=torch.uint8, device=dev)
@@ -455,11 +557,13 @@ def cobs_scores(problem: Problem, q, k_pages, pool: int, *, workspace=None, stre
     """Second-order block scores [batch, h_q, max_nr, max_nk] fp32."""
     import torch
     d = problem.dims(pool, 0.0)
+    c = problem.for_tensors(q)
+    problem.check_pages(k_pages)
     out = torch.empty((problem.c.batch, problem.c.h_q, d.max_nr, d.max_nk), dtype=torch.float32, device=q.device)
     ws_bytes = cosa_cobs_workspace_size(problem.c, pool)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-    cosa_cobs_scores(problem.c, q.data_ptr(), k_pages.data_ptr(), pool, out.data_ptr(), workspace.data_ptr(),
+    cosa_cobs_scores(c, q.data_ptr(), k_pages.data_ptr(), pool, out.data_ptr(), workspace.data_ptr(),
                      workspace.numel(), _stream(stream))
     return out
 
@@ -471,14 +575,18 @@ def osk_decode(problem: Problem, q, k_pages, v_pages, order, count, tau: float, 
     import torch
     dev = q.device
     d = problem.dims()
-    o = torch.empty_like(q) if out is None else out
+    problem.check_pages(k_pages)
+    problem.check_pages(v_pages, "v_pages")
+    problem.check_lists(order, count, dev)
+    o = problem.new_rows(q) if out is None else out
+    c = problem.for_tensors(q, o)
     vis = torch.empty((problem.c.batch, problem.c.h_q, d.max_nq), dtype=torch.int32, device=dev)
     skp = torch.empty_like(vis)
     ls = torch.empty((problem.c.h_q, d.total_q), dtype=torch.float32, device=dev) if lse else None
     ws_bytes = cosa_osk_decode_workspace_size(problem.c, n_splits)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    cosa_osk_decode(problem.c, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), order.data_ptr(),
+    cosa_osk_decode(c, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), order.data_ptr(),
                     count.data_ptr(), int(order.shape[3]), problem.group, tau, n_splits, o.data_ptr(),
                     vis.data_ptr(), skp.data_ptr(), _ptr(ls), workspace.data_ptr(), workspace.numel(),
                     _stream(stream))
@@ -493,6 +601,7 @@ def union_order(problem: Problem, order, count, *, union_kmax=None, stream=None)
     query block); returns dict(order, count)."""
     import torch
     d = problem.dims()
+    problem.check_lists(order, count, order.device)
     uk = d.max_nk if union_kmax is None else int(union_kmax)
     uo = torch.empty((problem.c.batch, problem.c.h_kv, d.max_nq, uk), dtype=torch.int32, device=order.device)
     uc = torch.empty(uo.shape[:3], dtype=torch.int32, device=order.device)
@@ -506,9 +615,12 @@ def block_mass(problem: Problem, q, k_pages, lse, *, stream=None):
     given the rows' log-sum-exp from ``dense_attention(..., lse=True)``."""
     import torch
     d = problem.dims()
+    c = problem.for_tensors(q)
+    problem.check_pages(k_pages)
+    _need(lse, "lse", shape=(problem.c.h_q, d.total_q), dtype=torch.float32, device=q.device)
     mass = torch.empty((problem.c.batch, problem.c.h_q, d.max_nq, d.max_nk), dtype=torch.float32,
                        device=q.device)
-    cosa_block_mass(problem.c, q.data_ptr(), k_pages.data_ptr(), lse.data_ptr(), mass.data_ptr(),
+    cosa_block_mass(c, q.data_ptr(), k_pages.data_ptr(), lse.data_ptr(), mass.data_ptr(),
                     _stream(stream))
     return mass
 

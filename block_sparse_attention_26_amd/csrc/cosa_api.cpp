@@ -45,6 +45,43 @@ int n_causal(int qb, int B, int Lq, int Lk) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Element strides of q and o (0 = contiguous).
+int64_t q_tok(const cosa_problem* p) { return p->q_stride_tok ? p->q_stride_tok : (int64_t)p->h_q * p->head_dim; }
+int64_t q_head(const cosa_problem* p) { return p->q_stride_head ? p->q_stride_head : p->head_dim; }
+int64_t o_tok(const cosa_problem* p) { return p->o_stride_tok ? p->o_stride_tok : (int64_t)p->h_q * p->head_dim; }
+int64_t o_head(const cosa_problem* p) { return p->o_stride_head ? p->o_stride_head : p->head_dim; }
+
+// Strides in 16-byte units (the kernels move q and o rows in 16-byte pieces)
+// and an o layout in which no two elements share memory.
+cosa_status check_strides(const cosa_problem* p) {
+  const int64_t unit = p->dtype == COSA_BF16 ? 8 : 4;
+  const int64_t v[4] = {p->q_stride_tok, p->q_stride_head, p->o_stride_tok, p->o_stride_head};
+  const char* name[4] = {"q_stride_tok", "q_stride_head", "o_stride_tok", "o_stride_head"};
+  for (int i = 0; i < 4; ++i)
+    if (v[i] < 0 || v[i] % unit != 0)
+      return fail(COSA_ERR_INVALID_ARG, "%s (%lld) must be >= 0 and a multiple of %lld elements (16 bytes)",
+                  name[i], (long long)v[i], (long long)unit);
+  // the output dimensions with more than one entry, by increasing stride
+  struct Dim { int64_t stride, n; } dims[2] = {{o_tok(p), p->host_cu_seqlens_q[p->batch]}, {o_head(p), p->h_q}};
+  if (dims[0].stride > dims[1].stride) std::swap(dims[0], dims[1]);
+  int nd = 0;
+  Dim live[2];
+  for (const Dim& d : dims)
+    if (d.n > 1) live[nd++] = d;
+  if (nd >= 1 && live[0].stride < p->head_dim)
+    return fail(COSA_ERR_INVALID_ARG, "o strides overlap: a stride (%lld) below head_dim (%d)",
+                (long long)live[0].stride, p->head_dim);
+  if (nd == 2 && live[1].stride < live[0].stride * live[0].n)
+    return fail(COSA_ERR_INVALID_ARG, "o strides overlap: stride %lld < %lld x %lld", (long long)live[1].stride,
+                (long long)live[0].stride, (long long)live[0].n);
+  return COSA_OK;
+}
+
+cosa_status check_aligned(const void* ptr, const char* what) {
+  if (((uintptr_t)ptr & 15) != 0) return fail(COSA_ERR_INVALID_ARG, "%s must be 16-byte aligned", what);
+  return COSA_OK;
+}
+
 cosa_status validate(const cosa_problem* p) {
   if (!p) return fail(COSA_ERR_INVALID_ARG, "problem is NULL");
   if (p->batch < 1) return fail(COSA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", p->batch);
@@ -78,7 +115,7 @@ cosa_status validate(const cosa_problem* p) {
       return fail(COSA_ERR_INVALID_ARG, "sequence %d needs %lld KV blocks > max_blocks_k (%d)", b,
                   (long long)cdiv(lk, p->block), p->max_blocks_k);
   }
-  return COSA_OK;
+  return check_strides(p);
 }
 
 void compute_dims(const cosa_problem* p, int pool, double budget, cosa_dims_t* d) {
@@ -133,6 +170,10 @@ cosa::SeqArgs seq_args(const cosa_problem* p, const cosa_dims_t& d) {
   s.num_pages = p->num_pages;
   s.max_nq = d.max_nq;
   s.max_nk = d.max_nk;
+  s.q_tok = q_tok(p);
+  s.q_head = q_head(p);
+  s.o_tok = o_tok(p);
+  s.o_head = o_head(p);
   return s;
 }
 
@@ -166,6 +207,7 @@ cosa_status run_attention(const cosa_problem* p, const void* q, const void* k, c
   cosa_status st = validate(p);
   if (st != COSA_OK) return st;
   if (!q || !k || !v || !o) return fail(COSA_ERR_INVALID_ARG, "q, k_pages, v_pages and o must be non-NULL");
+  if ((st = check_aligned(q, "q")) != COSA_OK || (st = check_aligned(o, "o")) != COSA_OK) return st;
   const bool masked = !dense && mask_words > 0;
   if (masked) {
     if (!mask || !visited || !skipped)
@@ -264,6 +306,13 @@ cosa_status cosa_dims(const cosa_problem* problem, int32_t pool, double budget, 
   return ok();
 }
 
+size_t cosa_kap_kmax(const cosa_problem* problem, double budget) {
+  if (validate(problem) != COSA_OK || !(budget > 0.0 && budget <= 1.0)) return 0;
+  cosa_dims_t d;
+  compute_dims(problem, 0, budget, &d);
+  return (size_t)d.kmax;
+}
+
 size_t cosa_kap_workspace_size(const cosa_problem* problem, int32_t pool, int32_t with_scores) {
   if (validate(problem) != COSA_OK || check_pool(problem, pool) != COSA_OK) return 0;
   return kap_ws_size(problem, pool, with_scores != 0);
@@ -282,6 +331,7 @@ static cosa_status run_kap(const cosa_problem* problem, const void* q, const voi
   if (!q || !(k_pages || pooled_keys) || !order || !hrm || !count)
     return fail(COSA_ERR_INVALID_ARG, pooled_keys ? "q, pooled_keys, order, hrm and count must be non-NULL"
                                                   : "q, k_pages, order, hrm and count must be non-NULL");
+  if ((st = check_aligned(q, "q")) != COSA_OK) return st;
   cosa_dims_t d;
   compute_dims(problem, pool, budget, &d);
   if (kmax < d.kmax)
@@ -436,6 +486,7 @@ cosa_status cosa_cobs_scores(const cosa_problem* problem, const void* q, const v
   if (st != COSA_OK) return st;
   if ((st = check_pool(problem, pool)) != COSA_OK) return st;
   if (!q || !k_pages || !scores) return fail(COSA_ERR_INVALID_ARG, "q, k_pages and scores must be non-NULL");
+  if ((st = check_aligned(q, "q")) != COSA_OK) return st;
   if (problem->dtype != COSA_BF16) return fail(COSA_ERR_UNSUPPORTED, "second-order scores are built for bf16 only");
   const size_t need = cosa_cobs_workspace_size(problem, pool);
   if (!workspace || workspace_bytes < need)
@@ -509,6 +560,7 @@ cosa_status cosa_osk_decode(const cosa_problem* problem, const void* q, const vo
   if (!q || !k_pages || !v_pages || !o || !order || !count || !visited || !skipped)
     return fail(COSA_ERR_INVALID_ARG, "q, k_pages, v_pages, o, order, count, visited and skipped must be non-NULL");
   if (p->dtype != COSA_BF16) return fail(COSA_ERR_UNSUPPORTED, "the decode walk is built for bf16 only");
+  if ((st = check_aligned(q, "q")) != COSA_OK || (st = check_aligned(o, "o")) != COSA_OK) return st;
   if (kmax < 1) return fail(COSA_ERR_INVALID_ARG, "kmax must be >= 1 (got %d)", kmax);
   if (group != p->h_q / p->h_kv)
     return fail(COSA_ERR_INVALID_ARG, "group (%d) must equal h_q / h_kv (%d)", group, p->h_q / p->h_kv);
@@ -559,6 +611,7 @@ cosa_status cosa_block_mass(const cosa_problem* problem, const void* q, const vo
   if (st != COSA_OK) return st;
   if (!q || !k_pages || !lse || !mass)
     return fail(COSA_ERR_INVALID_ARG, "q, k_pages, lse and mass must be non-NULL");
+  if ((st = check_aligned(q, "q")) != COSA_OK) return st;
   if (problem->dtype != COSA_BF16) return fail(COSA_ERR_UNSUPPORTED, "block mass is built for bf16 only");
   cosa_dims_t d;
   compute_dims(problem, 0, 0.0, &d);

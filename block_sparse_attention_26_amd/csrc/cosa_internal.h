@@ -26,6 +26,8 @@ struct SeqArgs {
   const int32_t* block_table;   // [batch, max_blocks_k]
   int32_t batch, h_q, h_kv, group, max_blocks_k, num_pages;
   int32_t max_nq, max_nk;
+  // element strides of q and o: token, head (head_dim is contiguous)
+  int64_t q_tok, q_head, o_tok, o_head;
 };
 
 // Ordered-skip / dense attention launch.

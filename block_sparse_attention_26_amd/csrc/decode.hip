@@ -95,7 +95,8 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_decode_kernel(DecodeArgs a) {
 
   bf16x8 qf[QREGS];
   {
-    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)q0 * sq.h_q + g * G + l32) * D + hl * 8;
+    // columns past the group's heads load nothing; their address is the group's first head
+    const uint16_t* qp = (const uint16_t*)a.q + (int64_t)q0 * sq.q_tok + (int64_t)(g * G + (col_ok ? l32 : 0)) * sq.q_head + hl * 8;
 #pragma unroll
     for (int ks = 0; ks < QREGS; ++ks) {
       const uint4 x = col_ok ? *(const uint4*)(qp + ks * 16) : make_uint4(0, 0, 0, 0);
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(256) void osk_decode_merge(DecodeArgs a) {
     for (int s = 0; s < S; ++s) l_star += part[s * (D + 2) + D + 1];
   }
   const float inv = l_star > 0.f ? 1.f / l_star : (l_star == l_star ? 0.f : l_star);
-  uint16_t* orow = (uint16_t*)a.o + ((size_t)q0 * sq.h_q + h) * D;
+  uint16_t* orow = (uint16_t*)a.o + (int64_t)q0 * sq.o_tok + (int64_t)h * sq.o_head;
 #pragma unroll
   for (int i = 0; i < (D + 63) / 64; ++i)
     if (lane + 64 * i < D) orow[lane + 64 * i] = __builtin_bit_cast(uint16_t, (__bf16)(o[i] * inv));

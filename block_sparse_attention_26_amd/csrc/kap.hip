@@ -90,13 +90,14 @@ __global__ __launch_bounds__(kThreads) void kap_pool_q(KapArgs a) {
   const float inv_cnt = 1.f / (float)(hi - lo);
   const int chunks = sq.h_q * D / 8;
   for (int c = threadIdx.x; c < chunks; c += kThreads) {
+    const int64_t cin = (int64_t)(c / (D / 8)) * sq.q_head + (c % (D / 8)) * 8;  // this chunk within a token
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     // eight tokens' loads in flight at a time; the sum stays in token order
     int tok = lo;
     for (; tok + 8 <= hi; tok += 8) {
       float x[8][8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) load8<BF16>(a.q, (size_t)(q0 + tok + u) * sq.h_q * D + (size_t)c * 8, x[u]);
+      for (int u = 0; u < 8; ++u) load8<BF16>(a.q, (size_t)((int64_t)(q0 + tok + u) * sq.q_tok + cin), x[u]);
 #pragma unroll
       for (int u = 0; u < 8; ++u)
 #pragma unroll
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void kap_pool_q(KapArgs a) {
     }
     for (; tok < hi; ++tok) {
       float x[8];
-      load8<BF16>(a.q, (size_t)(q0 + tok) * sq.h_q * D + (size_t)c * 8, x);
+      load8<BF16>(a.q, (size_t)((int64_t)(q0 + tok) * sq.q_tok + cin), x);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += x[i];
     }

@@ -60,7 +60,9 @@ __global__ __launch_bounds__(2 * BLK) void block_mass_kernel(MassArgs a) {
 
   bf16x8 qf[QREGS];
   {
-    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(q0 + qb * BLK + row) * sq.h_q + h) * D + hl * 8;
+    // rows past the sequence end load nothing; their address is the block's first row
+    const int qrow = row_valid ? row : 0;
+    const uint16_t* qp = (const uint16_t*)a.q + (int64_t)(q0 + qb * BLK + qrow) * sq.q_tok + (int64_t)h * sq.q_head + hl * 8;
 #pragma unroll
     for (int ks = 0; ks < QREGS; ++ks) {
       const uint4 x = row_valid ? *(const uint4*)(qp + ks * 16) : make_uint4(0, 0, 0, 0);

@@ -221,7 +221,8 @@ __global__ __launch_bounds__(2 * BLK, 1) void osk_kernel(OskArgs a) {  // 2*BLK 
   bf16x8 qf16[BF16 ? C::QREGS : 1];
   float qf32[BF16 ? 1 : C::QREGS];
   {
-    const size_t qoff = ((size_t)(q0 + qb * BLK + row) * sq.h_q + h) * D;
+    // rows past the sequence end load nothing; their address is the block's first row
+    const int64_t qoff = (int64_t)(q0 + qb * BLK + (row_valid ? row : 0)) * sq.q_tok + (int64_t)h * sq.q_head;
     if constexpr (BF16) {
       const uint16_t* qp = (const uint16_t*)a.q + qoff + hl * 8;
 #pragma unroll
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(2 * BLK, 1) void osk_kernel(OskArgs a) {  // 2*BLK 
   float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (bad) inv = __builtin_nanf("");
   if (row_valid) {
-    const size_t ooff = ((size_t)(q0 + qb * BLK + row) * sq.h_q + h) * D;
+    const int64_t ooff = (int64_t)(q0 + qb * BLK + row) * sq.o_tok + (int64_t)h * sq.o_head;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll

@@ -156,7 +156,9 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
   // ---- query fragments (B operand of S^T = K Q^T) -------------------------
   bf16x8 qf[QREGS];
   {
-    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(q0 + qb * BLK + row) * sq.h_q + h) * D + hl * 8;
+    // rows past the sequence end load nothing; their address is the block's first row
+    const int qrow = row_valid ? row : 0;
+    const uint16_t* qp = (const uint16_t*)a.q + (int64_t)(q0 + qb * BLK + qrow) * sq.q_tok + (int64_t)h * sq.q_head + hl * 8;
 #pragma unroll
     for (int ks = 0; ks < QREGS; ++ks) {
       const uint4 x = row_valid ? *(const uint4*)(qp + ks * 16) : make_uint4(0, 0, 0, 0);
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void osk_bf16_kernel(OskArgs a) {
   float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (bad) inv = __builtin_nanf("");
   if (row_valid) {
-    const size_t ooff = ((size_t)(q0 + qb * BLK + row) * sq.h_q + h) * D;
+    const int64_t ooff = (int64_t)(q0 + qb * BLK + row) * sq.o_tok + (int64_t)h * sq.o_head;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll

@@ -24,9 +24,16 @@
  *    outputs from run to run (no atomics in any accumulation).
  *  - Calls are reentrant; the error message is thread-local.
  *
- * Layouts (element counts, row-major, all contiguous):
+ * Layouts (element counts, row-major):
  *  q, o        [total_q, h_q, head_dim]   sequences packed back to back;
  *              sequence b owns rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1.
+ *              Element (t, h, c) of q sits at q + t*q_stride_tok +
+ *              h*q_stride_head + c (likewise o with the o_ strides), so q may
+ *              be a view into a larger tensor, e.g. the query part of a fused
+ *              QKV projection, read in place (zero-copy access to the
+ *              caller's tensors, CompactAttention page, execution stage).
+ *              head_dim is always contiguous. Every other tensor argument is
+ *              contiguous in the layout stated for it.
  *  k/v pages   [num_pages, h_kv, block, head_dim]: KV-head-major pages, one
  *              page per (logical KV block) so each (page, KV head) slab is
  *              contiguous (layout of the CompactAttention page, execution
@@ -80,6 +87,16 @@ typedef struct cosa_problem {
                                        in [0, num_pages)                       */
   const int32_t* host_cu_seqlens_q; /* host copy of cu_seqlens_q              */
   const int32_t* host_seqlens_k;    /* host copy of seqlens_k                  */
+  /* Element strides of q and o between consecutive tokens and heads; 0 takes
+   * the contiguous value (tok: h_q*head_dim, head: head_dim). Each must be
+   * >= 0 and a multiple of 16 bytes (8 bf16 or 4 fp32 elements), and the q
+   * and o pointers 16-byte aligned (COSA_ERR_INVALID_ARG otherwise). The o
+   * strides must not make two output elements share memory: the smaller
+   * stride (with more than one token or head along it) is >= head_dim and
+   * the larger >= the smaller times that extent. q may alias itself freely
+   * (it is only read). */
+  int64_t q_stride_tok, q_stride_head;
+  int64_t o_stride_tok, o_stride_head;
 } cosa_problem;
 
 /* Padded extents derived from a problem (see cosa_dims). */
@@ -103,6 +120,10 @@ cosa_status cosa_validate(const cosa_problem* problem);
  * same purpose (kmax is then 0). */
 cosa_status cosa_dims(const cosa_problem* problem, int32_t pool, double budget,
                       cosa_dims_t* out /* host */);
+
+/* Host-only: width of the proxy's order lists under `budget` in (0, 1]
+ * (cosa_dims(problem, 0, budget).kmax); 0 for an invalid problem or budget. */
+size_t cosa_kap_kmax(const cosa_problem* problem, double budget);
 
 /* Bytes of device workspace cosa_kap_order needs; `with_scores` = 0 when the
  * caller passes its own proxy_scores buffer (the scores then live there).

@@ -267,3 +267,103 @@ def test_pooled_key_entry_points_reject_bad_arguments():
     with pytest.raises(cosa.CosaError) as e:  # workspace too small
         cosa.cosa_kap_order_pooled(p.c, ptr, ptr, 16, 0.1, ptr, ptr, ptr, 26, None, None, ptr, 16, None)
     assert e.value.status == -3
+
+
+def test_kap_kmax_matches_dims():
+    _lib_or_skip()
+    p = _problem((131072,))
+    for beta, want in [(0.05, 52), (0.1, 103), (0.25, 256), (1.0, 1024)]:
+        assert cosa.cosa_kap_kmax(p.c, beta) == want == p.dims(16, beta).kmax
+    assert cosa.cosa_kap_kmax(p.c, 0.0) == 0 and cosa.cosa_kap_kmax(p.c, 1.5) == 0
+
+
+class AlignedBuf:
+    """Host memory whose address is 16-byte aligned plus `shift` bytes."""
+
+    def __init__(self, shift=0, nbytes=256):
+        self._buf = (ctypes.c_uint8 * (nbytes + 32))()
+        base = ctypes.addressof(self._buf)
+        self.addr = ((base + 15) & ~15) + shift
+
+    def data_ptr(self):
+        return self.addr
+
+
+@pytest.mark.parametrize("fields,ok", [
+    (dict(q_stride_tok=3 * 32 * 128, q_stride_head=128), True),          # q inside a fused QKV row
+    (dict(q_stride_tok=128, q_stride_head=1024 * 128), True),            # heads-major q
+    (dict(o_stride_tok=128, o_stride_head=1024 * 128), True),            # heads-major o
+    (dict(q_stride_tok=-8), False),
+    (dict(q_stride_head=4), False),                                       # 8 bytes: not a 16-byte multiple
+    (dict(o_stride_tok=32 * 128 + 4), False),
+    (dict(o_stride_head=64), False),                                      # heads overlap within a token
+    (dict(o_stride_tok=128 * 16, o_stride_head=128), False),             # tokens overlap the 32 heads
+    (dict(o_stride_tok=0, o_stride_head=128 * 1024), False),             # default tok stride < 32 heads apart
+])
+def test_strides_validated(fields, ok):
+    _lib_or_skip()
+    p = _problem((1024,))
+    for k_, v_ in fields.items():
+        setattr(p.c, k_, v_)
+    st = p.validate()
+    assert (st == 0) == ok, (fields, st, cosa.cosa_last_error())
+    if not ok:
+        assert st == -1 and "stride" in cosa.cosa_last_error()
+
+
+def test_fp32_stride_unit_is_four_elements():
+    _lib_or_skip()
+    p = _problem((1024,), h_q=1, h_kv=1, d=64, B=64, dtype=cosa.COSA_F32)
+    p.c.q_stride_tok = 68  # 272 bytes
+    assert p.validate() == 0
+    p.c.q_stride_tok = 66
+    assert p.validate() == -1
+
+
+def test_misaligned_q_and_o_rejected():
+    _lib_or_skip()
+    p = _problem((1024,))
+    good, bad = AlignedBuf(0), AlignedBuf(2)
+    any_ = FakeDev(64, 64)
+    ws = AlignedBuf(0)
+    # proxy: q checked before the workspace
+    with pytest.raises(cosa.CosaError, match="q must be 16-byte aligned"):
+        cosa.cosa_kap_order(p.c, bad.data_ptr(), any_.data_ptr(), 16, 0.1, any_.data_ptr(), any_.data_ptr(),
+                            any_.data_ptr(), 103, None, None, ws.data_ptr(), 0, None)
+    # walks: q and o
+    for q_, o_, what in [(bad, good, "q"), (good, bad, "o")]:
+        with pytest.raises(cosa.CosaError, match=f"{what} must be 16-byte aligned"):
+            cosa.cosa_osk_attention(p.c, q_.data_ptr(), any_.data_ptr(), any_.data_ptr(), any_.data_ptr(),
+                                    any_.data_ptr(), 103, 4, 0.0, o_.data_ptr(), any_.data_ptr(),
+                                    any_.data_ptr(), None, None, None)
+        with pytest.raises(cosa.CosaError, match=f"{what} must be 16-byte aligned"):
+            cosa.cosa_dense_attention(p.c, q_.data_ptr(), any_.data_ptr(), any_.data_ptr(), o_.data_ptr(), None,
+                                      None)
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The torch helpers check shapes, dtypes and devices before any pointer
+    reaches the library (CPU tensors stand in: every check here fires first)."""
+    import torch
+    _lib_or_skip()
+    p = _problem((1024,))
+    q = torch.zeros((1024, 32, 128), dtype=torch.bfloat16)
+    k = torch.zeros((8, 8, 128, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="shape"):
+        cosa.kap_order(p, q[:1000], k, 16, 0.1)
+    with pytest.raises(ValueError, match="dtype"):
+        cosa.kap_order(p, q.float(), k, 16, 0.1)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        cosa.kap_order(p, q, k, 16, 0.1)
+    with pytest.raises(ValueError, match="head_dim"):
+        p._rows_view(torch.zeros((128, 32, 1024), dtype=torch.bfloat16).transpose(0, 2), "q")
+    with pytest.raises(ValueError, match="k_pages has shape"):
+        cosa.dense_attention(p, q, k[:4], k)
+    order = torch.zeros((1, 8, 8, 103), dtype=torch.int32)
+    with pytest.raises(ValueError, match="count has shape"):
+        p.check_lists(order, torch.zeros((1, 8, 7), dtype=torch.int32))
+    with pytest.raises(ValueError, match="order has dtype"):
+        p.check_lists(order.long(), torch.zeros((1, 8, 8), dtype=torch.int32))
+    with pytest.raises(ValueError, match="order must be"):
+        p.check_lists(order[0], torch.zeros((1, 8, 8), dtype=torch.int32))
+    assert p.check_lists(order, torch.zeros((1, 8, 8), dtype=torch.int32)) == 103
