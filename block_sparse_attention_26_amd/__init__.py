@@ -33,7 +33,7 @@ __all__ = [
     "cosa_osk_attention_masked", "cosa_block_mass", "cosa_union_order",
     "cosa_osk_decode", "cosa_osk_decode_workspace_size", "cosa_kap_rank", "cosa_cobs_scores",
     "cosa_cobs_workspace_size", "cosa_kap_pool_keys", "cosa_kap_order_pooled", "cosa_kap_kmax",
-    "kap_order", "pool_keys", "osk_attention", "dense_attention", "mask_from_order", "order_from_mask",
+    "cosa_osk_decode_noalloc", "kap_order", "pool_keys", "osk_attention", "dense_attention", "mask_from_order", "order_from_mask",
     "osk_attention_masked", "mask_words_for", "block_mass", "union_order", "osk_decode", "kap_rank",
     "cobs_scores",
     "COSA_F32", "COSA_BF16", "EXPORTED_SYMBOLS",
@@ -51,6 +51,7 @@ EXPORTED_SYMBOLS = (
     "cosa_osk_attention_masked", "cosa_block_mass", "cosa_union_order",
     "cosa_osk_decode", "cosa_osk_decode_workspace_size", "cosa_kap_rank", "cosa_cobs_scores",
     "cosa_cobs_workspace_size", "cosa_kap_pool_keys", "cosa_kap_order_pooled", "cosa_kap_kmax",
+    "cosa_osk_decode_noalloc",
 )
 
 
@@ -117,6 +118,7 @@ def load():
         "cosa_cobs_workspace_size": (sz, [P, i32]),
         "cosa_cobs_scores": (i32, [P, vp, vp, i32, vp, vp, sz, vp]),
         "cosa_osk_decode": (i32, [P, vp, vp, vp, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "cosa_osk_decode_noalloc": (i32, [P, vp, vp, vp, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, vp]),
         "cosa_status_string": (ctypes.c_char_p, [i32]),
         "cosa_last_error": (ctypes.c_char_p, []),
         "cosa_version": (i32, []),
@@ -237,6 +239,13 @@ def cosa_osk_decode(problem, q, k_pages, v_pages, order, count, kmax, group, ski
     _check(load().cosa_osk_decode(ctypes.byref(problem), q, k_pages, v_pages, order, count, int(kmax),
                                   int(group), float(skip_threshold), int(n_splits), o, visited, skipped,
                                   lse, workspace, int(workspace_bytes), stream))
+
+
+def cosa_osk_decode_noalloc(problem, q, k_pages, v_pages, order, count, kmax, group, skip_threshold, n_splits,
+                            o, visited, skipped, lse, stream) -> None:
+    _check(load().cosa_osk_decode_noalloc(ctypes.byref(problem), q, k_pages, v_pages, order, count, int(kmax),
+                                          int(group), float(skip_threshold), int(n_splits), o, visited, skipped,
+                                          lse, stream))
 
 
 def cosa_union_order(problem, order, count, kmax, union_order, union_count, union_kmax, stream) -> None:

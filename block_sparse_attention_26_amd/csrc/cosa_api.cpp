@@ -5,10 +5,19 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "../../include/cosa.h"
 #include "cosa_internal.h"
+
+// Fixed device scratch of the allocation-free decode entry point
+// (cosa_osk_decode_noalloc): each GPU the library runs on holds its own copy
+// of this array, at its own address, from the module's load until the process
+// ends. Host code never passes `scratch` itself to a kernel (on the host the
+// name is only a stand-in); it passes the device address looked up below.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -180,6 +189,30 @@ cosa::SeqArgs seq_args(const cosa_problem* p, const cosa_dims_t& d) {
 cosa_status hip_result(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(COSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+cosa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(COSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(COSA_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch table holds", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(COSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return COSA_OK;
 }
 
 int32_t min_mask_words(const cosa_problem* p) {
@@ -549,11 +582,13 @@ size_t cosa_osk_decode_workspace_size(const cosa_problem* problem, int32_t n_spl
   return decode_ws_size(problem, n_splits);
 }
 
-cosa_status cosa_osk_decode(const cosa_problem* problem, const void* q, const void* k_pages,
-                            const void* v_pages, const int32_t* order, const int32_t* count,
-                            int32_t kmax, int32_t group, float skip_threshold, int32_t n_splits,
-                            void* o, int32_t* visited, int32_t* skipped, float* lse,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+// The decode step over a caller's workspace, or (fixed_scratch) over this
+// library's static per-device scratch array.
+static cosa_status run_decode(const cosa_problem* problem, const void* q, const void* k_pages,
+                              const void* v_pages, const int32_t* order, const int32_t* count,
+                              int32_t kmax, int32_t group, float skip_threshold, int32_t n_splits,
+                              void* o, int32_t* visited, int32_t* skipped, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream, bool fixed_scratch) {
   cosa_status st = validate(problem);
   if (st != COSA_OK) return st;
   const cosa_problem* p = problem;
@@ -574,12 +609,22 @@ cosa_status cosa_osk_decode(const cosa_problem* problem, const void* q, const vo
       return fail(COSA_ERR_INVALID_ARG, "sequence %d has %d query tokens; a decode step has at most one", b,
                   p->host_cu_seqlens_q[b + 1] - p->host_cu_seqlens_q[b]);
   const size_t need = decode_ws_size(p, n_splits);
-  if (!workspace || workspace_bytes < need)
-    return fail(COSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
-  if (((uintptr_t)workspace & 255) != 0) return fail(COSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (fixed_scratch) {
+    if (need > kScratchBytes)
+      return fail(COSA_ERR_UNSUPPORTED,
+                  "the decode step needs %zu bytes of scratch (batch %d x h_q %d x n_splits %d partial "
+                  "results), more than the fixed %zu-byte scratch of the allocation-free entry point; "
+                  "use cosa_osk_decode with a workspace",
+                  need, p->batch, p->h_q, n_splits, kScratchBytes);
+  } else {
+    if (!workspace || workspace_bytes < need)
+      return fail(COSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    if (((uintptr_t)workspace & 255) != 0) return fail(COSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
   cosa_dims_t d;
   compute_dims(p, 0, 0.0, &d);
   if (d.total_q == 0 || d.max_nq == 0) return ok();
+  if (fixed_scratch && (st = scratch_of_current_device(&workspace)) != COSA_OK) return st;
   cosa::DecodeArgs a{};
   a.seq = seq_args(p, d);
   a.q = q;
@@ -603,6 +648,23 @@ cosa_status cosa_osk_decode(const cosa_problem* problem, const void* q, const vo
   a.skip_on = skip_threshold > 0.f ? 1 : 0;
   a.skip_thr_raw = a.skip_on ? (float)(log((double)skip_threshold) / (double)p->softmax_scale) : 0.f;
   return hip_result(cosa::launch_osk_decode(a, p->head_dim, p->block, (hipStream_t)stream), "decode launch");
+}
+
+cosa_status cosa_osk_decode(const cosa_problem* problem, const void* q, const void* k_pages,
+                            const void* v_pages, const int32_t* order, const int32_t* count,
+                            int32_t kmax, int32_t group, float skip_threshold, int32_t n_splits,
+                            void* o, int32_t* visited, int32_t* skipped, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return run_decode(problem, q, k_pages, v_pages, order, count, kmax, group, skip_threshold, n_splits, o,
+                    visited, skipped, lse, workspace, workspace_bytes, stream, false);
+}
+
+cosa_status cosa_osk_decode_noalloc(const cosa_problem* problem, const void* q, const void* k_pages,
+                                    const void* v_pages, const int32_t* order, const int32_t* count,
+                                    int32_t kmax, int32_t group, float skip_threshold, int32_t n_splits,
+                                    void* o, int32_t* visited, int32_t* skipped, float* lse, void* stream) {
+  return run_decode(problem, q, k_pages, v_pages, order, count, kmax, group, skip_threshold, n_splits, o,
+                    visited, skipped, lse, nullptr, 0, stream, true);
 }
 
 cosa_status cosa_block_mass(const cosa_problem* problem, const void* q, const void* k_pages,

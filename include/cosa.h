@@ -283,6 +283,25 @@ cosa_status cosa_osk_decode(const cosa_problem* problem, const void* q, const vo
                             void* o, int32_t* visited, int32_t* skipped, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the decode
+ * step of cosa_osk_decode, same arguments and results bit for bit, with the
+ * per-segment partial results kept in a fixed scratch array inside the
+ * library instead of a caller's workspace. The call allocates nothing.
+ * Limit: cosa_osk_decode_workspace_size(problem, n_splits) must not exceed
+ * 32 MiB (33554432 bytes), e.g. batch 64 x 64 query heads x 15 segments at
+ * head_dim 128; larger problems are rejected with COSA_ERR_UNSUPPORTED before
+ * any launch. Every call on one GPU uses that GPU's single array, which keeps
+ * the last call's contents (no part of it needs clearing: every partial
+ * result the merge reads is written by the same call), so calls that can
+ * overlap on one GPU (different streams or threads) race: order them on one
+ * stream. The array (32 MiB per GPU) is held from the library's first use on
+ * a device until the process ends. */
+cosa_status cosa_osk_decode_noalloc(const cosa_problem* problem, const void* q, const void* k_pages,
+                                    const void* v_pages, const int32_t* order, const int32_t* count,
+                                    int32_t kmax, int32_t group, float skip_threshold, int32_t n_splits,
+                                    void* o, int32_t* visited, int32_t* skipped, float* lse, void* stream);
+
 /* ---- Binary block masks (comparison modes) -----------------------------------
  * The CoSA summary contrasts its computation-order list (§2.1) with the
  * binary masks of earlier proxies, and its page-remapped walk (§2.3,

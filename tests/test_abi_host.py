@@ -367,3 +367,22 @@ def test_binding_rejects_mismatched_tensors():
     with pytest.raises(ValueError, match="order must be"):
         p.check_lists(order[0], torch.zeros((1, 8, 8), dtype=torch.int32))
     assert p.check_lists(order, torch.zeros((1, 8, 8), dtype=torch.int32)) == 103
+
+
+def test_noalloc_decode_rejects_before_any_launch():
+    """The allocation-free decode step refuses problems whose partial results
+    exceed its fixed 32 MiB scratch, and bad arguments, on the host."""
+    _lib_or_skip()
+    p = _problem((1,) * 8, (600,) * 8, h_q=8, h_kv=2)
+    buf, any_ = AlignedBuf(0), FakeDev(64, 64)
+    args = lambda n_splits, group=4: (p.c, buf.data_ptr(), any_.data_ptr(), any_.data_ptr(), any_.data_ptr(),
+                                      any_.data_ptr(), 8, group, 0.0, n_splits, buf.data_ptr(), any_.data_ptr(),
+                                      any_.data_ptr(), None, None)
+    assert cosa.cosa_osk_decode_workspace_size(p.c, 1024) > 32 << 20
+    with pytest.raises(cosa.CosaError, match="scratch") as ei:
+        cosa.cosa_osk_decode_noalloc(*args(1024))
+    assert ei.value.status == -2
+    with pytest.raises(cosa.CosaError, match="group"):
+        cosa.cosa_osk_decode_noalloc(*args(4, group=3))
+    with pytest.raises(cosa.CosaError, match="n_splits"):
+        cosa.cosa_osk_decode_noalloc(*args(0))
