@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcosa.so")
-SOURCES = ["cosa_api.cpp", "osk.hip", "osk_bf16.hip", "kap.hip", "mask.hip", "mass.hip", "decode.hip", "cobs.hip"]
+SOURCES = ["cosa_api.cpp", "osk.hip", "osk_bf16.hip", "kap.hip", "kap_fused.hip", "mask.hip", "mass.hip", "decode.hip",
+           "cobs.hip"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -39,6 +40,12 @@ FLAGS = [
 ]
 
 
+# per-source additions: the fused proxy pass keeps up to 128 proxy scores per
+# lane in registers, indexed by fully unrolled loops of up to 128 steps, which
+# exceed clang's default size limit for a requested full unroll
+EXTRA = {"kap_fused.hip": ["-mllvm", "-pragma-unroll-threshold=1000000"]}
+
+
 def hipcc() -> str:
     cand = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(cand) and shutil.which(cand) is None:
@@ -49,7 +56,7 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(OUT, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-    cmd = [hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

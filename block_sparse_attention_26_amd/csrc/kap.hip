@@ -27,6 +27,7 @@
 #include <type_traits>
 
 #include "cosa_internal.h"
+#include "kap_common.h"
 
 namespace cosa {
 namespace {
@@ -35,8 +36,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kThreads = 256;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
   return __builtin_bit_cast(float, h16 << 16);
@@ -685,26 +684,6 @@ __global__ __launch_bounds__(kThreads, 2) void kap_score_grp(KapArgs a) {
   __builtin_amdgcn_s_waitcnt(0);  // no copy is in flight when the workgroup's LDS is released
 }
 
-// ---- exp32: the proxy's exponential, as specified ---------------------------
-// 0 unless x >= -87; t = x*fp32(log2 e); n = rint(t); f = t - n;
-// Horner over c_k = fp32(ln2^k / k!), k = 7..0; result p * 2^n.
-__device__ float exp32(float x) {
-#pragma clang fp contract(off)
-  if (!(x >= -87.0f)) return 0.0f;
-  const float t = x * __builtin_bit_cast(float, 0x3FB8AA3Bu);
-  const float n = __builtin_rintf(t);
-  const float f = t - n;
-  float p = __builtin_bit_cast(float, 0x377FE5FEu);            // ln2^7/7!
-  p = f * p; p = p + __builtin_bit_cast(float, 0x39218489u);   // ln2^6/6!
-  p = f * p; p = p + __builtin_bit_cast(float, 0x3AAEC3FFu);   // ln2^5/5!
-  p = f * p; p = p + __builtin_bit_cast(float, 0x3C1D955Bu);   // ln2^4/4!
-  p = f * p; p = p + __builtin_bit_cast(float, 0x3D635847u);   // ln2^3/3!
-  p = f * p; p = p + __builtin_bit_cast(float, 0x3E75FDF0u);   // ln2^2/2!
-  p = f * p; p = p + __builtin_bit_cast(float, 0x3F317218u);   // ln2
-  p = f * p; p = p + 1.0f;
-  return __builtin_ldexpf(p, (int)n);
-}
-
 // ---- MaxNorm, HRM, block score, flag-grouped sort, budget (R5-R10) ---------
 // One workgroup per (sequence, KV group, query block), longest rows first.
 
@@ -830,79 +809,6 @@ __global__ __launch_bounds__(kThreads) void kap_score_decode(KapArgs a) {
   }
 }
 
-// ---- descending bitonic sort of 256*E unique 64-bit keys -------------------
-// Thread t holds entries t*E .. t*E+E-1 in registers. Stages whose partner is
-// in the same thread swap registers, stages within a wave exchange through
-// cross-lane shuffles, and only stages across waves go through LDS (`lds`
-// holds 256*E keys). The network's result is the unique descending order.
-__device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, int m) {
-  const int lo = __shfl_xor((int)(uint32_t)v, m, 64);
-  const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m, 64);
-  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
-template <int E>
-__device__ __forceinline__ void bitonic_desc(unsigned long long (&x)[E], unsigned long long* lds, int tid) {
-  constexpr int N = kThreads * E;
-  const int lane = tid & 63;
-  for (int k = 2; k <= N; k <<= 1) {
-    for (int j = k >> 1; j >= E; j >>= 1) {
-      if (j < 64 * E) {  // partner: the same register of lane ^ (j / E)
-        const int m = j / E;
-        const bool lower = (lane & m) == 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const unsigned long long y = shfl_xor64(x[e], m);
-          const bool desc = ((tid * E + e) & k) == 0;
-          const bool take_max = lower == desc;
-          x[e] = take_max ? (x[e] > y ? x[e] : y) : (x[e] < y ? x[e] : y);
-        }
-      } else {  // partner in another wave
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < E; ++e) lds[tid * E + e] = x[e];
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int i = tid * E + e;
-          const unsigned long long y = lds[i ^ j];
-          const bool take_max = ((i & j) == 0) == ((i & k) == 0);
-          x[e] = take_max ? (x[e] > y ? x[e] : y) : (x[e] < y ? x[e] : y);
-        }
-      }
-    }
-#pragma unroll
-    for (int jj = E / 2; jj >= 1; jj >>= 1) {  // partner in the same thread
-      if (jj <= (k >> 1)) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          if ((e & jj) == 0) {
-            const int q = e | jj;
-            const bool desc = ((tid * E + e) & k) == 0;
-            const unsigned long long lo = x[e], hi = x[q];
-            const bool sw = desc ? (lo < hi) : (lo > hi);
-            x[e] = sw ? hi : lo;
-            x[q] = sw ? lo : hi;
-          }
-        }
-      }
-    }
-  }
-}
-
-// sorts keys[0 .. N) (N = 256*E) descending, leaving the result in keys
-template <int E>
-__device__ __forceinline__ void sort_keys_desc(unsigned long long* keys, int tid) {
-  unsigned long long x[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) x[e] = keys[tid * E + e];
-  bitonic_desc<E>(x, keys, tid);
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < E; ++e) keys[tid * E + e] = x[e];
-  __syncthreads();
-}
-
 // the rank pass's sort size for lists of up to max_nk blocks (a power of two,
 // at least one key per thread) and its dynamic LDS: keys, then row maxima
 __host__ __device__ inline int rank_sort_size(int max_nk) {
@@ -1015,9 +921,7 @@ __global__ __launch_bounds__(kThreads) void kap_rank_sort(KapArgs a) {
           }
         }
       }
-      key = ((unsigned long long)(flag ? 1u : 0u) << 63) |
-            ((unsigned long long)__builtin_bit_cast(uint32_t, s) << 32) |
-            (unsigned long long)(0xFFFFFFFFu - (uint32_t)kb);
+      key = rank_key(flag, s, kb);
       if (bs) bs[kb] = s;
     }
     keys[kb] = key;
@@ -1027,13 +931,7 @@ __global__ __launch_bounds__(kThreads) void kap_rank_sort(KapArgs a) {
   __syncthreads();
 
   // descending sort (padding keys are 0, below every real key)
-  switch (npad / kThreads) {
-    case 1: sort_keys_desc<1>(keys, tid); break;
-    case 2: sort_keys_desc<2>(keys, tid); break;
-    case 4: sort_keys_desc<4>(keys, tid); break;
-    case 8: sort_keys_desc<8>(keys, tid); break;
-    default: sort_keys_desc<16>(keys, tid); break;
-  }
+  sort_keys_desc_any(keys, npad, tid);
 
   int kcnt = (int)ceil(a.budget * (double)n - 1e-9);
   kcnt = max(1, min(n, kcnt));
@@ -1065,6 +963,7 @@ hipError_t launch_all(const KapArgs& a, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int per = BLK / a.pool;
+  if (kap_fused_eligible(a, BF16 ? 1 : 0, BLK)) return launch_kap_fused(a, D, BLK, stream);
   if (BF16 && kap_decode_scores(a.max_nr, sq.group, per, 1)) {  // one pooled row: heads as columns
     const int64_t nchunk = ((int64_t)sq.max_nk * per + kDecodeKeys - 1) / kDecodeKeys;
     const int64_t g3 = nchunk * sq.h_kv * sq.batch;
