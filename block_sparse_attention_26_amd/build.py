@@ -20,8 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcosa.so")
-SOURCES = ["cosa_api.cpp", "osk.hip", "osk_bf16.hip", "kap.hip", "kap_fused.hip", "mask.hip", "mass.hip", "decode.hip",
-           "cobs.hip"]
+SOURCES = ["cosa_api.cpp", "osk.hip", "osk_bf16.hip", "kap.hip", "mask.hip", "mass.hip", "decode.hip", "cobs.hip"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -40,10 +39,8 @@ FLAGS = [
 ]
 
 
-# per-source additions: the fused proxy pass keeps up to 128 proxy scores per
-# lane in registers, indexed by fully unrolled loops of up to 128 steps, which
-# exceed clang's default size limit for a requested full unroll
-EXTRA = {"kap_fused.hip": ["-mllvm", "-pragma-unroll-threshold=1000000"]}
+# per-source additions to the flags
+EXTRA = {}
 
 
 def hipcc() -> str:

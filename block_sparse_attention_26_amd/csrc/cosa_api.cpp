@@ -150,19 +150,12 @@ cosa_status check_pool(const cosa_problem* p, int pool) {
   return COSA_OK;
 }
 
-// The proxy takes the fused pass (P in registers, no P or row-maxima
-// workspace) for these shapes, else the score pass + rank pass route.
-bool proxy_fused(const cosa_problem* p, int pool, const cosa_dims_t& d) {
-  return cosa::kap_fused_shape(p->dtype, p->block / pool, p->h_q / p->h_kv, d.max_nk, d.max_nr);
-}
-
 size_t kap_ws_size(const cosa_problem* p, int pool, bool with_scores) {
   cosa_dims_t d;
   compute_dims(p, pool, 0.0, &d);
   const size_t es = p->dtype == COSA_BF16 ? 2 : 4;
   size_t sz = align256((size_t)p->batch * d.max_nr * p->h_q * p->head_dim * es);
   sz += align256((size_t)p->num_pages * p->h_kv * (p->block / pool) * p->head_dim * es);
-  if (proxy_fused(p, pool, d)) return sz;
   sz += align256((size_t)p->batch * p->h_q * d.max_nr * sizeof(float));  // row maxima of P
   if (with_scores) sz += align256((size_t)p->batch * p->h_q * d.max_nr * d.max_nk * sizeof(float));
   return sz;
@@ -402,14 +395,12 @@ static cosa_status run_kap(const cosa_problem* problem, const void* q, const voi
   ws += align256((size_t)problem->num_pages * problem->h_kv * (problem->block / pool) *
                  problem->head_dim * es);
   // the score pass reduces rows of P to their maxima when blocks hold 4..32
-  // pooled keys (not in its decode shape); otherwise the rank pass does. The
-  // fused pass needs neither the maxima nor P (it writes P only when asked).
+  // pooled keys (not in its decode shape); otherwise the rank pass does
   const int per = problem->block / pool;
   const bool decode_scores = cosa::kap_decode_scores(d.max_nr, problem->h_q / problem->h_kv, per, problem->dtype);
-  const bool fused = proxy_fused(problem, pool, d);
-  a.row_max = (!fused && per >= 4 && per <= 32 && !decode_scores) ? (float*)ws : nullptr;
-  if (!fused) ws += align256((size_t)problem->batch * problem->h_q * d.max_nr * sizeof(float));
-  a.scores = own_scores ? (fused ? nullptr : (float*)ws) : proxy_scores;
+  a.row_max = (per >= 4 && per <= 32 && !decode_scores) ? (float*)ws : nullptr;
+  ws += align256((size_t)problem->batch * problem->h_q * d.max_nr * sizeof(float));
+  a.scores = own_scores ? (float*)ws : proxy_scores;
   a.fill_scores = own_scores ? 0 : 1;
   a.block_scores = block_scores;
   a.order = order;

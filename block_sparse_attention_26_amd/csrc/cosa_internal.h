@@ -85,19 +85,6 @@ inline bool kap_decode_scores(int max_nr, int group, int per, int dtype) {
   return max_nr == 1 && group <= 32 && per >= 4 && per <= 32 && dtype == 1;
 }
 
-// The fused proxy pass (scores through sort in one workgroup per list row,
-// P kept in registers) takes bf16 problems whose blocks hold 4, 8 or 16
-// pooled keys, whose list rows have at most 32 (query head, pooled row)
-// pairs, with at most kFusedMaxBlocks KV blocks per sequence and more than
-// one pooled query row; the others take the score pass + rank pass route.
-constexpr int kFusedMaxBlocks = 1024;
-inline bool kap_fused_shape(int dtype, int per, int group, int max_nk, int max_nr) {
-  return dtype == 1 && (per == 4 || per == 8 || per == 16) && group * per <= 32 && max_nk <= kFusedMaxBlocks &&
-         !kap_decode_scores(max_nr, group, per, dtype);
-}
-bool kap_fused_eligible(const KapArgs& a, int dtype, int block);
-hipError_t launch_kap_fused(const KapArgs& a, int head_dim, int block, hipStream_t stream);
-
 // Mask <-> list conversions (one wave per row of batch * h_kv * max_nq).
 struct MaskArgs {
   SeqArgs seq;

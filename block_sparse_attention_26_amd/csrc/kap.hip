@@ -579,6 +579,8 @@ __global__ __launch_bounds__(kThreads, 2) void kap_score_grp(KapArgs a) {
   // A operand: key row kt*32 + l32, logical chunk 2*ks + hl
   const int k_swz = l32 % CH;
   float rmx = kNegInf;       // raw row maximum over the computed keys
+  float pend[16];            // scaled block maxima waiting for their row segment to complete
+  int npend = 0;             // steps in the ring since the last write
   // s_waitcnt with vmcnt <= (NSTAGE-2)*CPW (expcnt and lgkmcnt at their
   // maxima): vector memory operations complete in issue order, and when the
   // copies of the NSTAGE-2 following steps were issued after this step's, at
@@ -660,22 +662,52 @@ __global__ __launch_bounds__(kThreads, 2) void kap_score_grp(KapArgs a) {
         bm[kt] = vmax(t01, t23);
       }
     }
-    // the step's NB block maxima of this lane's row: the two lane halves
-    // write one half each
-    auto store = [&](auto nb_c) {
-      constexpr int HALF = decltype(nb_c)::value / 2;
-      float* prow = P + (int64_t)my_r * sq.max_nk + (j0 >> lper) + hl * HALF;
-      const int room = kb_end - (j0 >> lper) - hl * HALF;  // blocks of this half still covered
+    // the step's NB block maxima of this lane's row (the two lane halves hold
+    // one half each) wait in a register ring until a 32-block (128-byte)
+    // segment of the row is complete, which both halves then write in the
+    // same store instructions: lines of P are written whole, not a few bytes
+    // per step (partly written lines evicted early were written twice)
+    auto stash = [&](auto nb_c) {
+      constexpr int NB = decltype(nb_c)::value;  // blocks per step
+      constexpr int HALF = NB / 2;
+      constexpr int F = 32 / NB;                 // steps per segment
+      static_assert(F * HALF == 16, "ring size");
 #pragma unroll
-      for (int i = 0; i < HALF; ++i)
-        if (i < room) prow[i] = (hl ? bm[HALF + i] : bm[i]) * a.scale;
+      for (int t = 0; t < F - 1; ++t)
+#pragma unroll
+        for (int i = 0; i < HALF; ++i) pend[t * HALF + i] = pend[(t + 1) * HALF + i];
+#pragma unroll
+      for (int i = 0; i < HALF; ++i) pend[(F - 1) * HALF + i] = (hl ? bm[HALF + i] : bm[i]) * a.scale;
+      ++npend;
+      const int kb_next = (j0 >> lper) + NB;  // the first block after this step
+      if ((kb_next & 31) == 0 || j0 + STEP >= j_hi) {
+        if (r_ok) {
+#pragma unroll
+          for (int t = 0; t < F; ++t) {
+            if (t >= F - npend) {  // slot t: the step starting at block kb_next - (F - t) * NB
+              const int kb = kb_next - (F - t) * NB + hl * HALF;
+              float* dst = P + (int64_t)my_r * sq.max_nk + kb;
+              const int room = kb_end - kb;  // blocks of this half still covered
+              if (HALF % 4 == 0 && room >= HALF && ((uintptr_t)dst & 15) == 0) {
+#pragma unroll
+                for (int i = 0; i < HALF; i += 4)
+                  *(float4*)(dst + i) = make_float4(pend[t * HALF + i], pend[t * HALF + i + 1],
+                                                    pend[t * HALF + i + 2], pend[t * HALF + i + 3]);
+              } else {
+#pragma unroll
+                for (int i = 0; i < HALF; ++i)
+                  if (i < room) dst[i] = pend[t * HALF + i];
+              }
+            }
+          }
+        }
+        npend = 0;
+      }
     };
-    if (r_ok) {
-      if (per == 4) store(std::integral_constant<int, STEP / 4>{});
-      else if (per == 8) store(std::integral_constant<int, STEP / 8>{});
-      else if (per == 16) store(std::integral_constant<int, STEP / 16>{});
-      else store(std::integral_constant<int, STEP / 32>{});
-    }
+    if (per == 4) stash(std::integral_constant<int, STEP / 4>{});
+    else if (per == 8) stash(std::integral_constant<int, STEP / 8>{});
+    else if (per == 16) stash(std::integral_constant<int, STEP / 16>{});
+    else stash(std::integral_constant<int, STEP / 32>{});
   }
   if (wave_on) {
     if (a.row_max && hl == 0 && r_ok) a.row_max[((int64_t)b * sq.h_q + h) * a.max_nr + my_r] = rmx * a.scale;
@@ -963,7 +995,6 @@ hipError_t launch_all(const KapArgs& a, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int per = BLK / a.pool;
-  if (kap_fused_eligible(a, BF16 ? 1 : 0, BLK)) return launch_kap_fused(a, D, BLK, stream);
   if (BF16 && kap_decode_scores(a.max_nr, sq.group, per, 1)) {  // one pooled row: heads as columns
     const int64_t nchunk = ((int64_t)sq.max_nk * per + kDecodeKeys - 1) / kDecodeKeys;
     const int64_t g3 = nchunk * sq.h_kv * sq.batch;

@@ -109,10 +109,9 @@ def test_workspace_size_and_argument_errors():
     p = _problem((2048,))
     with_scores = cosa.cosa_kap_workspace_size(p.c, 16, True)
     without = cosa.cosa_kap_workspace_size(p.c, 16, False)
-    # GQA 4, 8 pooled keys per block: the fused pass keeps P in registers, so
-    # only pooled Q (16 rows x 32 heads x 128 x 2B per 256 tokens) and pooled K
-    assert with_scores == without == 128 * 32 * 128 * 2 + 16 * 8 * 8 * 128 * 2
-    # GQA 8 (64 rows per list) takes the score pass + rank pass: row maxima, and P
+    # pooled Q (16 rows x 32 heads x 128 x 2B per 256 tokens), pooled K, row maxima, and P
+    assert without == 128 * 32 * 128 * 2 + 16 * 8 * 8 * 128 * 2 + 32 * 128 * 4
+    assert with_scores == without + 32 * 128 * 16 * 4
     p8 = _problem((2048,), h_q=64)
     with_scores = cosa.cosa_kap_workspace_size(p8.c, 16, True)
     without = cosa.cosa_kap_workspace_size(p8.c, 16, False)
