@@ -35,6 +35,7 @@ METRIC = "ms/layer + effective TFLOP/s, 128K causal prefill at 10% budget; speed
 
 WORKLOADS = {
     # name: (config number, default budget, description)
+    "cfg1": (1, 0.25, "1K causal prefill, 1q/1kv head, d64, fp32, block 64, pool 8, 4 planted keys"),
     "cfg3": (3, 0.10, "128K causal prefill, 32q/8kv heads, d128, bf16, block 128, pool 16, 32 needle blocks/KV head"),
     "cfg2": (2, 0.10, "32K causal prefill, 32q/8kv heads, d128, bf16, block 128, pool 16"),
     "cfg4": (4, 0.10, "4K chunk over a 64K paged cache (shuffled pages), 32q/8kv, d128, bf16"),
@@ -60,6 +61,8 @@ def parse():
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="only time large bf16 matrix products (torch.matmul, the vendor GEMM): the "
                          "MFMA rate the box sustains, against which the walk's fraction of peak is read")
+    ap.add_argument("--no-gemm", action="store_true",
+                    help="skip the vendor-GEMM rate measured beside the walk (one 16384^3 product size)")
     return ap.parse_args()
 
 
@@ -76,9 +79,9 @@ def blas_info():
     return {"vendor": "unknown", "version": None, "threads": os.cpu_count() or 1, "library": ""}
 
 
-def gemm_ceiling(sizes=((8192, 8192, 8192), (16384, 16384, 16384)), reps=20):
+def gemm_ceiling(sizes=((8192, 8192, 8192), (16384, 16384, 16384)), reps=20, emit=True):
     """bf16 C = A.B with torch.matmul (hipBLASLt on ROCm) at large square sizes:
-    TFLOP/s from HIP events around `reps` back-to-back products after a warm-up."""
+    TFLOP/s from HIP events around each of `reps` products after a warm-up."""
     import torch
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -108,7 +111,9 @@ def gemm_ceiling(sizes=((8192, 8192, 8192), (16384, 16384, 16384)), reps=20):
         print(f"[gemm] {m}x{n}x{k} bf16: median {med:.3f} ms = {out[-1]['tflops_median']:.0f} TFLOP/s "
               f"(best {out[-1]['tflops_best']:.0f})", file=sys.stderr, flush=True)
         del a, b, c
-    print(json.dumps({"gemm_ceiling": out, "peak_bf16_tflops": MFMA_BF16_PEAK_TFLOPS}), flush=True)
+    if emit:
+        print(json.dumps({"gemm_ceiling": out, "peak_bf16_tflops": MFMA_BF16_PEAK_TFLOPS}), flush=True)
+    return out
 
 
 OSK_SOURCE = os.path.join(ROOT, "block_sparse_attention_26_amd", "csrc", "osk_bf16.hip")
@@ -134,9 +139,11 @@ def profiled_traffic():
 
 
 def cpu_baseline(case, kap_count, seconds_target=20.0):
-    """Time the oracle on KV group 0: its whole proxy, then its ordered walk
-    over evenly spaced query blocks until about `seconds_target` seconds of
-    CPU work, and extrapolate to the whole layer."""
+    """Time the oracle on KV group 0 of the first sequence: its whole proxy,
+    then its ordered walk over evenly spaced query blocks until about
+    `seconds_target` seconds of CPU work, and extrapolate to the whole layer
+    (the proxy by its pooled score-matrix size summed over the sequences, the
+    walk by listed blocks)."""
     import numpy as np
     from oracle import kap as okap, osk as oosk, layout
 
@@ -146,7 +153,7 @@ def cpu_baseline(case, kap_count, seconds_target=20.0):
     B, p = case.block, case.pool
     T = case.seqlens_q[0]
     Lk = int(case.seqlens_k[0])
-    qg = case.q[:, :G].float().numpy()
+    qg = case.q[: T, :G].float().numpy()  # sequence 0 (packed first)
     kg = case.kv_contiguous(0, "k")[:, 0:1].float().numpy()
     vg = case.kv_contiguous(0, "v")[:, 0:1].float().numpy()
     kmax = layout.kmax(B, [T], [Lk], case.budget)
@@ -167,12 +174,14 @@ def cpu_baseline(case, kap_count, seconds_target=20.0):
     # every list of the layer (all KV groups); each is walked by G query heads,
     # as the sampled lists of group 0 were
     total_blocks = int(kap_count.sum())
-    layer_s = t_kap * case.h_kv + t_osk * total_blocks / max(1, done_blocks)
+    kap_scale = sum(lq * int(lk) for lq, lk in zip(case.seqlens_q, case.seqlens_k.tolist())) / (T * Lk)
+    layer_s = t_kap * case.h_kv * kap_scale + t_osk * total_blocks / max(1, done_blocks)
     return {
         "layer_seconds": layer_s,
         "cores": int(cores),
         "blas": blas,
-        "sample": (f"oracle (numpy fp64) proxy of KV group 0 over all {T} tokens ({t_kap:.1f} s, x{case.h_kv} groups) "
+        "sample": (f"oracle (numpy fp64) proxy of KV group 0 over all {T} tokens of sequence 0 ({t_kap:.1f} s, "
+                   f"x{case.h_kv} groups x{kap_scale:.2f} for the batch) "
                    f"+ ordered walk of KV group 0 ({G} query heads) over {len(done_q)} query blocks "
                    f"({done_blocks} listed blocks, {t_osk:.1f} s), extrapolated by listed-block count "
                    f"to all {total_blocks} lists of the layer"),
@@ -305,6 +314,12 @@ def main():
     osk_tflops = osk_flops / (osk_ms * 1e-3) / 1e12
     peak = MFMA_BF16_PEAK_TFLOPS if case.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
 
+    gemm = None
+    if not args.no_gemm and case.dtype == "bf16":
+        g = gemm_ceiling(sizes=((16384, 16384, 16384),), reps=10, emit=False)[0]
+        gemm = g["tflops_median"]
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
@@ -355,7 +370,8 @@ def main():
         "visited_head_blocks": visited,
         "skipped_head_blocks": skipped,
         "roofline": {
-            "kernel": "osk_bf16_kernel<128,128> (ordered-skip walk)",
+            "kernel": ("osk_bf16_kernel<128,128> (ordered-skip walk)" if case.dtype == "bf16"
+                       else f"osk_kernel<fp32,{D},{B}> (ordered-skip walk)"),
             "bound": "mfma",
             "achieved": osk_tflops,
             "peak": peak,
@@ -363,6 +379,10 @@ def main():
             "frac": osk_tflops / peak,
             "traffic": profiled_traffic() if args.workload == "cfg3" and abs(case.budget - 0.1) < 1e-12 else None,
             "algorithmic_flops_per_launch": osk_flops,
+            # the vendor GEMM (torch.matmul, 16384^3 bf16) timed in the same
+            # process: what the box sustains on plain matrix work
+            "measured_gemm_tflops": gemm,
+            "frac_of_measured_gemm": (osk_tflops / gemm) if gemm else None,
         },
         "cpu_baseline": cpu,
     }

@@ -848,9 +848,12 @@ __host__ __device__ inline int rank_sort_size(int max_nk) {
   while (n < max_nk) n <<= 1;
   return n;
 }
+// (the row maxima padded to a whole number of the key loop's 16-row chunks)
+constexpr int kRankChunk = 16;
 inline size_t rank_lds_bytes(const KapArgs& a, int block) {
   const int nr = a.seq.group * (block / a.pool);  // G * (B/p) pooled rows per list
-  return (size_t)rank_sort_size(a.seq.max_nk) * sizeof(unsigned long long) + (size_t)nr * sizeof(float);
+  const int nr_pad = (nr + kRankChunk - 1) / kRankChunk * kRankChunk;
+  return (size_t)rank_sort_size(a.seq.max_nk) * sizeof(unsigned long long) + (size_t)nr_pad * sizeof(float);
 }
 
 template <int BLK>
@@ -927,17 +930,37 @@ __global__ __launch_bounds__(kThreads) void kap_rank_sort(KapArgs a) {
       float s = 0.0f;
       bool flag = false;
       // heads ascending, then rows ascending; the loads of a chunk of rows are
-      // issued together, the sum stays sequential
-      constexpr int CHUNK = 16;
+      // issued together, and so are the chunk's row maxima (four 16-byte LDS
+      // reads, one wait per chunk instead of one per term); the sum stays
+      // sequential
+      constexpr int CHUNK = kRankChunk;
+      // element offset of row (head g*G + ri / nrow, pooled row r0 + ri % nrow),
+      // advanced row by row (no division per term)
+      int64_t roff = ((int64_t)g * G * a.max_nr + r0) * sq.max_nk;
+      int rr = 0;
+      const int64_t next_head = (int64_t)(a.max_nr - nrow + 1) * sq.max_nk;
       for (int r0c = 0; r0c < NR; r0c += CHUNK) {
-        float xs[CHUNK];
+        float xs[CHUNK], rm[CHUNK];
 #pragma unroll
         for (int c = 0; c < CHUNK; ++c) {
           const int ri = r0c + c;
           if (ri < NR) {
-            const int h = g * G + ri / nrow, r = r0 + ri % nrow;
-            xs[c] = Pb[((int64_t)h * a.max_nr + r) * sq.max_nk + kb];
+            xs[c] = Pb[roff + kb];
+            if (++rr == nrow) {
+              rr = 0;
+              roff += next_head;
+            } else {
+              roff += sq.max_nk;
+            }
           }
+        }
+#pragma unroll
+        for (int q = 0; q < CHUNK / 4; ++q) {
+          const float4 m4 = *(const float4*)(rmax + r0c + 4 * q);  // padded: in bounds
+          rm[4 * q] = m4.x;
+          rm[4 * q + 1] = m4.y;
+          rm[4 * q + 2] = m4.z;
+          rm[4 * q + 3] = m4.w;
         }
 #pragma unroll
         for (int c = 0; c < CHUNK; ++c) {
@@ -946,7 +969,7 @@ __global__ __launch_bounds__(kThreads) void kap_rank_sort(KapArgs a) {
             float dlt;
             {
 #pragma clang fp contract(off)
-              dlt = xs[c] - rmax[ri];
+              dlt = xs[c] - rm[c];
               s = s + exp32(dlt);
             }
             flag |= (dlt == 0.0f);
