@@ -7,10 +7,11 @@ must agree with it bit for bit.
 
 Checked on outputs the oracle computes one by one: list rows (all of them at
 10%, every fourth query block and the last two otherwise) bit-exact against
-the oracle fed the GPU's proxy scores; the output and skip sets of four KV
-groups at sixteen query blocks (first two, last two, twelve evenly spaced)
-against the oracle's ordered walk; at 10% also the dense kernel on sampled
-query blocks; per-layer list totals against their closed forms.
+the oracle fed the GPU's proxy scores; the output and skip sets against the
+oracle's ordered walk at 10% for 64 query blocks (first two, last two, sixty
+evenly spaced) of every query head, otherwise for four KV groups at sixteen
+query blocks; at 10% also the dense kernel on sampled query blocks;
+per-layer list totals against their closed forms.
 """
 import numpy as np
 import pytest
@@ -46,9 +47,12 @@ def test_full_128k(variant):
     rows = None if variant == "b10" else [sorted(set(range(0, nq, 4)) | {nq - 2, nq - 1})]
     say(case.name, "lists")
     check_lists(case, g, budget, rows=rows)
-    qbs = sample_qbs(nq, 12)
-    say(case.name, "walk of four KV groups at the sampled query blocks")
-    mx, mean, n_amb, n_skip = _walk_groups(case, g, qbs)
+    if variant == "b10":  # 64 query blocks of every head
+        qbs, groups = sample_qbs(nq, 60), tuple(range(case.h_kv))
+    else:
+        qbs, groups = sample_qbs(nq, 12), GROUPS
+    say(case.name, f"walk of {len(groups)} KV groups at {len(qbs)} query blocks")
+    mx, mean, n_amb, n_skip = _walk_groups(case, g, qbs, groups)
     say(case.name, f"walk: max err {mx:.3e} mean {mean:.3e}, {n_skip} skipped, {n_amb} ambiguous")
     if sink is not None:
         assert n_skip > 0, "aligned sinks must make the walk skip tiles"
@@ -57,7 +61,6 @@ def test_full_128k(variant):
         check_dense(case, g["dev"], [[0, 1, nq // 2, nq - 1]])
 
 
-def _walk_groups(case, g, qbs):
-    """check_walk restricted to GROUPS (the oracle's walk is per KV group)."""
-    import gpu_common as gc
-    return gc.check_walk(case, g, [qbs], groups=GROUPS)
+def _walk_groups(case, g, qbs, groups):
+    """check_walk restricted to some KV groups (the oracle's walk is per KV group)."""
+    return check_walk(case, g, [qbs], groups=groups)
