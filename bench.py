@@ -69,6 +69,7 @@ def parse():
 def blas_info():
     """Vendor, version and thread count of the BLAS numpy calls into."""
     try:
+        import numpy  # noqa: F401  (loads the BLAS that threadpoolctl then finds)
         from threadpoolctl import threadpool_info
         for i in threadpool_info():
             if i.get("user_api") == "blas":
@@ -330,6 +331,7 @@ def main():
             "value": dense_flops / cb["layer_seconds"] / 1e12,
             "unit": "TFLOP/s (effective, dense-causal-equivalent)",
             "cores": cb["cores"],
+            "blas": cb["blas"],
             "kind": "oracle",
             "sample": cb["sample"],
             "layer_seconds_extrapolated": cb["layer_seconds"],
