@@ -310,6 +310,7 @@ class Problem:
             host_seqlens_k=ctypes.cast(self._hlk, ctypes.c_void_p),
         )
         self.group = h_q // h_kv
+        self._dims = {}
 
     # -- tensor checks (shapes and dtypes the C ABI assumes) --------------------
     def torch_dtype(self):
@@ -375,7 +376,12 @@ class Problem:
                    host_seqlens_k=case.seqlens_k.tolist())
 
     def dims(self, pool: int = 0, budget: float = 0.0) -> cosa_dims_t:
-        return cosa_dims(self.c, pool, budget)
+        """Padded extents (cached: a Problem's shape does not change after construction)."""
+        key = (int(pool), float(budget))
+        d = self._dims.get(key)
+        if d is None:
+            d = self._dims[key] = cosa_dims(self.c, pool, budget)
+        return d
 
     def validate(self) -> int:
         return cosa_validate(self.c)
