@@ -58,6 +58,10 @@ CASES = {
     # phases of four, so the second phase holds only two
     "bf16-kv6-phases": _lr("bf16-kv6-phases", 26, [900, 300], [900, 700], hq=12, hkv=6, d=128, B=128, p=16,
                            per_sequence_seeds=True),
+    # a packed batch holding a sequence with no query token (its KV cache is
+    # not empty): empty lists, no output rows, nothing written for it
+    "bf16-empty-seq": _lr("bf16-empty-seq", 27, [600, 0, 900], [600, 500, 1200], hq=8, hkv=2, d=128, B=128, p=16,
+                          per_sequence_seeds=True, spare_pages=2, shuffle_pages=True),
 }
 
 
