@@ -141,9 +141,6 @@ struct DecodeArgs {
 hipError_t launch_osk(const OskArgs& a, int dtype, int head_dim, int block, bool dense,
                       hipStream_t stream);
 hipError_t launch_osk_bf16(const OskArgs& a, int head_dim, int block, bool dense, hipStream_t stream);
-// two-tile walk (osk_pp.hip): head_dim 128, block 128, even query-group size
-bool osk_pp_supported(int head_dim, int block, int group);
-hipError_t launch_osk_pp(const OskArgs& a, bool dense, hipStream_t stream);
 hipError_t launch_kap(const KapArgs& a, int dtype, int head_dim, int block, hipStream_t stream);
 // single stages: query pooling (bf16) and the rank/sort pass over given scores
 hipError_t launch_kap_pool_q(const KapArgs& a, int dtype, int head_dim, hipStream_t stream);
