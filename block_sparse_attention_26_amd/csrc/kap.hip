@@ -41,12 +41,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
   return __builtin_bit_cast(float, h16 << 16);
 }
 
-// 8 consecutive elements -> fp32
+// 8 consecutive elements -> fp32 (the pooling passes read each element once:
+// bf16 loads are non-temporal, which keeps the stream out of the way of cached data)
 template <bool BF16>
 __device__ __forceinline__ void load8(const void* base, size_t elem, float* out) {
   if constexpr (BF16) {
-    const uint4 x = *(const uint4*)((const uint16_t*)base + elem);
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+    const u32x4_nt x = __builtin_nontemporal_load((const u32x4_nt*)((const uint16_t*)base + elem));
+    const uint32_t w[4] = {x[0], x[1], x[2], x[3]};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       out[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
@@ -606,13 +608,28 @@ __global__ __launch_bounds__(kThreads, 2) void kap_score_grp(KapArgs a) {
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sc[kt][v] = 0.f;
+    // fragments of k-step ks+1 are read while the MFMAs of k-step ks run (order
+    // pinned: without it the reads were placed just before their MFMAs)
+    {
+      bf16x8 kf[2][KT];
 #pragma unroll
-    for (int ks = 0; ks < QREGS; ++ks) {
-      bf16x8 kf[KT];
+      for (int kt = 0; kt < KT; ++kt) kf[0][kt] = *(const bf16x8*)(kl + kt * 32 * ROWB + (((hl) ^ k_swz) << 4));
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) kf[kt] = *(const bf16x8*)(kl + kt * 32 * ROWB + (((2 * ks + hl) ^ k_swz) << 4));
+      for (int ks = 0; ks < QREGS; ++ks) {
+        if (ks + 1 < QREGS) {
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt], qf[ks], sc[kt], 0, 0, 0);
+          for (int kt = 0; kt < KT; ++kt)
+            kf[(ks + 1) & 1][kt] = *(const bf16x8*)(kl + kt * 32 * ROWB + (((2 * (ks + 1) + hl) ^ k_swz) << 4));
+        }
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks & 1][kt], qf[ks], sc[kt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, KT, 0);
+#pragma unroll
+      for (int ks = 0; ks < QREGS; ++ks) {
+        if (ks + 1 < QREGS) __builtin_amdgcn_sched_group_barrier(0x100, KT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, KT, 0);
+      }
     }
     // element v of tile kt: key j0 + kt*32 + 8*(v/4) + 4*hl + v%4; only steps
     // that reach the first row's causal edge or the key range end need the mask
@@ -945,7 +962,7 @@ __global__ __launch_bounds__(kThreads) void kap_rank_sort(KapArgs a) {
         for (int c = 0; c < CHUNK; ++c) {
           const int ri = r0c + c;
           if (ri < NR) {
-            xs[c] = Pb[roff + kb];
+            xs[c] = __builtin_nontemporal_load(Pb + roff + kb);  // P is read once: non-temporal
             if (++rr == nrow) {
               rr = 0;
               roff += next_head;
